@@ -1,0 +1,179 @@
+"""Throughput of the packed embedding pass on one MI355X.
+
+A step is one pass of the whole path over one batch of synthetic input: for
+the default workload, 64 packs of <= 2048 tokens (texts of log-uniform
+length in [8, 512], greedy packing; full-size 25-layer 768-d encoder with
+bf16 weights and matmul operands, fp32 accumulation), one tte_embed call per
+pack.  Token ids and weights are resident in HBM before timing starts.
+
+Prints ONE JSON line: tokens/s (every token of every text, BOS/EOS included),
+the roofline of the dominant kernel measured with HIP events on the model's
+stream inside the timed region, and the CPU oracle timed on a bounded sample
+of the same workload on the host's cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "encoded tokens/sec (25-layer 768-d encoder, ~2048-token packs) + % MFMA peak"
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3, "int8": 5000.0}
+DTYPE = {"bf16": "bf16", "fp32": "f32", "int8": "int8"}
+# flops per token of each GEMM class (H = 768, I = 3072): 2 * N * K
+GEMM_CLASSES = {"gemm_qkv": lambda H, I: 2 * 3 * H * H, "gemm_o": lambda H, I: 2 * H * H,
+                "gemm_geglu": lambda H, I: 2 * 2 * I * H, "gemm_o2": lambda H, I: 2 * H * I}
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(name, cfg, w, packs, budget_tokens):
+    """The oracle as it stands on a sample of the workload's first pack."""
+    import oracle
+    import threadpoolctl
+    pack = packs[0]
+    texts, n = [], 0
+    for b in range(pack.n_texts):
+        if n >= budget_tokens:
+            break
+        texts.append(b)
+        n += len(pack.text(b))
+    ids = np.concatenate([pack.text(b) for b in texts])
+    off = np.concatenate([[0], np.cumsum([len(pack.text(b)) for b in texts])])
+    t0 = time.perf_counter()
+    oracle.encode(cfg.as_dict(), w, ids, off)
+    dt = time.perf_counter() - t0
+    threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    return {"value": round(len(ids) / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {len(texts)} texts ({len(ids)} tokens) of pack 0, fp64 numpy, {dt:.1f}s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="full_bf16_packs2048")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=400)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kernel-events", action="store_true",
+                    help="time the steps without the per-launch events of the dominant kernel")
+    ap.add_argument("--breakdown", action="store_true", help="add an untimed step timing every kernel class")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import tte_inputs as ti
+    from transformer_text_embedding_amd import B, Model
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    dev = torch.device("cuda:0")
+    spec = ti.workload(a.workload)
+    cfg = spec["cfg"]
+    t0 = time.perf_counter()
+    w = ti.cached_storage_weights(cfg)
+    packs = ti.make_packs(a.workload)
+    log(f"inputs ready in {time.perf_counter() - t0:.1f}s: {len(packs)} packs, "
+        f"{sum(p.n_tokens for p in packs)} tokens")
+    max_tokens = max(p.n_tokens for p in packs)
+    model = Model(cfg, w, max_tokens=max_tokens, max_text_len=max(max_tokens, 512), max_texts=1024, device="cuda:0")
+    stream = torch.cuda.Stream(device=dev)
+    ids = [torch.from_numpy(p.ids).to(dev) for p in packs]
+    outs = [torch.empty((p.n_texts, cfg.hidden), dtype=torch.float32, device=dev) for p in packs]
+    offs = [B.int32_array(p.offsets) for p in packs]
+    L = B.lib()
+    h = model.handle
+    sh = stream.cuda_stream
+
+    def step():
+        for i, p in enumerate(packs):
+            st = L.tte_embed(h, ids[i].data_ptr(), p.n_tokens, offs[i], p.n_texts, outs[i].data_ptr(), sh)
+            if st != 0:
+                B.check(st)
+
+    torch.cuda.synchronize()
+    for _ in range(a.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("warmup done")
+
+    dominant = "gemm_geglu"
+    dom_bit = 1 << B.KERNEL_CLASSES.index(dominant)
+    if not a.no_kernel_events:
+        B.tte_profile_start(h, dom_bit, cfg.layers * len(packs) * a.steps + 16)
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter()
+    start.record(stream)
+    for _ in range(a.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    t_host = time.perf_counter() - t_host
+    ms_total = start.elapsed_time(end)
+    tokens_per_step = sum(p.n_tokens for p in packs)
+    value = tokens_per_step * a.steps / (ms_total / 1e3)
+    log(f"timed {a.steps} steps: {ms_total:.2f} ms on the stream, {t_host * 1e3:.2f} ms host")
+
+    roofline = None
+    H, I = cfg.hidden, cfg.intermediate
+    if not a.no_kernel_events:
+        prof = B.tte_profile_stop(h)
+        ms_dom, n_dom = prof[dominant]
+        flops = GEMM_CLASSES[dominant](H, I) * tokens_per_step * cfg.layers * a.steps
+        achieved = flops / (ms_dom / 1e3) / 1e12
+        peak = PEAK_TFLOPS[cfg.precision]
+        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak, 4), "traffic": None, "kernel": f"k_gemm ({dominant})",
+                    "launches": int(n_dom), "avg_launch_us": round(ms_dom * 1e3 / max(n_dom, 1), 2),
+                    "flops_per_launch_avg": int(flops / max(n_dom, 1))}
+
+    breakdown = None
+    if a.breakdown:
+        B.tte_profile_start(h, (1 << B.TTE_K_COUNT) - 1, 200 * len(packs) + 16)
+        step()
+        prof = B.tte_profile_stop(h)
+        breakdown = {}
+        for k, (ms, n) in prof.items():
+            if n == 0:
+                continue
+            entry = {"ms": round(ms, 3), "launches": int(n)}
+            if k in GEMM_CLASSES:
+                tf = GEMM_CLASSES[k](H, I) * tokens_per_step * cfg.layers / (ms / 1e3) / 1e12
+                entry["TFLOP/s"] = round(tf, 1)
+            breakdown[k] = entry
+
+    torch.cuda.synchronize()
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(ms_total / a.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[cfg.precision], "data": "synthetic",
+        "config": {"workload": a.workload, "packs_per_step": len(packs), "tokens_per_step": tokens_per_step,
+                   "pack_budget": spec.get("pack_budget"), "layers": cfg.layers, "hidden": cfg.hidden,
+                   "heads": cfg.heads, "intermediate": cfg.intermediate, "calls_per_step": len(packs)},
+        "roofline": roofline,
+    }
+    if breakdown is not None:
+        line["kernels"] = breakdown
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        line["cpu_baseline"] = cpu_baseline(a.workload, cfg, w, packs, a.cpu_sample_tokens)
+    model.close()
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,215 @@
+/*
+ * tte.h -- C ABI of the packed text-embedding encoder for MI355X (gfx950).
+ *
+ * The library computes the embedding pass described on the tensai
+ * "テキスト埋め込み" page (mattn.github.io/tensai/ja/embeddings):
+ *   - section 何が動くか, encoder paragraph: a ModernBERT encoder whose layers
+ *     are a bias-free LayerNorm, multi-head attention with RoPE and a GeGLU
+ *     feed-forward; layer 0 and every third layer after it attend over the
+ *     whole text (RoPE base 160000), the others only to the 64 tokens on
+ *     either side (base 10000);
+ *   - same section, pooling paragraph: the last layer's output is averaged
+ *     over each text and scaled to unit length;
+ *   - same section, packing paragraph: several texts are processed in one
+ *     pass, positions restart in every text and attention never crosses a
+ *     text, so a packed call returns the same vectors as one call per text;
+ *   - section 精度と量子化: the integer path rounds each activation row to
+ *     7 bits with one scale per row and uses the stored weight blocks as is.
+ *
+ * Conventions shared by every entry point:
+ *   - Every function returns a tte_status.  On failure nothing has been
+ *     enqueued on the stream and tte_last_error() (per calling thread) holds
+ *     a message; the model stays usable.
+ *   - Pointers named d_* are device pointers (HIP device memory), h_* are
+ *     host pointers.  The library never takes ownership of caller memory.
+ *   - Work is stream-ordered: results in d_* outputs are valid only once the
+ *     given stream (a hipStream_t passed as void*, NULL = default stream)
+ *     has reached the enqueued work.
+ *   - Matrices are row-major.  Activations are token-major [T, H].  Weights
+ *     are [out, in], so every projection is Y = X * W^T.
+ */
+#ifndef TTE_H
+#define TTE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TTE_OK = 0,
+  TTE_E_INVALID = 1,     /* bad argument: nothing was enqueued */
+  TTE_E_UNSUPPORTED = 2, /* valid but not implemented (e.g. head_dim != 64) */
+  TTE_E_NOMEM = 3,       /* workspace too small, or host allocation failed */
+  TTE_E_DEVICE = 4       /* no GPU, or a HIP runtime error */
+} tte_status;
+
+typedef enum {
+  TTE_FP32 = 0, /* fp32 weights and activations, fp32 matrix cores */
+  TTE_BF16 = 1, /* bf16 weights and matmul/attention operands, fp32 accumulate,
+                   fp32 residual stream, norms and softmax statistics */
+  TTE_INT8 = 2  /* int8 weight blocks of 32 inputs with fp32 scales; every
+                   weight matmul input rounded per row to 7 bits (|q| <= 63)
+                   with an fp32 row scale; int8 matrix cores, int32 sums per
+                   block; attention, norms and residual in fp32 */
+} tte_precision;
+
+/* Model shape and limits.  Defaults in parentheses are the page's values. */
+typedef struct {
+  int32_t vocab;
+  int32_t hidden;           /* H = n_heads * head_dim */
+  int32_t n_heads;
+  int32_t head_dim;         /* must be 64 */
+  int32_t intermediate;     /* I: the GeGLU up-projection has 2*I outputs */
+  int32_t n_layers;
+  int32_t global_every;     /* layer l is global iff l % global_every == 0 (3) */
+  int32_t window;           /* local layers: |i - j| <= window (64) */
+  float rope_base_global;   /* (160000) */
+  float rope_base_local;    /* (10000) */
+  float ln_eps;             /* (1e-5) */
+  int32_t max_tokens;       /* largest n_tokens of one tte_embed call */
+  int32_t max_text_len;     /* longest text (RoPE tables are sized by it) */
+  int32_t max_texts;        /* largest n_texts of one call */
+  int32_t precision;        /* tte_precision */
+} tte_config;
+
+/* Device pointers to one layer's weights, in the storage format of the
+ * precision: fp32 or bf16 (raw uint16 bits) arrays, or int8 codes with fp32
+ * scales [out, in/32] (the *_scale pointers are read only in TTE_INT8). */
+typedef struct {
+  const void* wqkv;  const float* wqkv_scale;  /* [3H, H]: rows Q, then K, then V; head j at rows j*64.. */
+  const void* wo;    const float* wo_scale;    /* [H, H] */
+  const void* wi;    const float* wi_scale;    /* [2I, H]: rows 0..I-1 pass through GELU, I..2I-1 gate */
+  const void* wo2;   const float* wo2_scale;   /* [H, I] */
+  const float* attn_norm;                      /* [H] fp32; NULL on layer 0 (no norm there) */
+  const float* mlp_norm;                       /* [H] fp32 */
+} tte_layer_weights;
+
+typedef struct {
+  const void* tok_emb; const float* tok_emb_scale; /* [vocab, H] (+ [vocab, H/32] scales in TTE_INT8) */
+  const float* emb_norm;                           /* [H] fp32 */
+  const float* final_norm;                         /* [H] fp32 */
+  const tte_layer_weights* layers;                 /* host array of n_layers entries, copied by tte_create */
+} tte_weights;
+
+typedef struct tte_model tte_model;
+
+/* Bytes of device workspace a model of this config needs (activations,
+ * per-token text bounds, RoPE tables, pooling partials).  *bytes is set on
+ * success. */
+tte_status tte_workspace_size(const tte_config* cfg, size_t* bytes);
+
+/* Create a model over BORROWED device weights and a BORROWED device
+ * workspace of at least tte_workspace_size bytes (256-byte aligned).  Both
+ * must outlive the model.  Writes the RoPE tables into the workspace
+ * (synchronously) and allocates a small pinned host staging area.  Several
+ * models may share one set of weights; use one model per concurrent stream.
+ * Returns TTE_E_DEVICE when no GPU is present. */
+tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_workspace,
+                      size_t workspace_bytes, tte_model** out);
+
+/* Embed one pack.  d_token_ids: int32 [n_tokens] on the device, the texts
+ * concatenated.  h_offsets: host int32 [n_texts + 1], offsets[0] = 0,
+ * strictly increasing (no empty text), offsets[n_texts] = n_tokens, every
+ * text at most max_text_len tokens, n_tokens <= max_tokens, n_texts <=
+ * max_texts.  The offsets are validated before anything is enqueued and
+ * copied, so the caller may reuse h_offsets when the call returns.
+ * d_out: fp32 [n_texts, H], one unit-norm vector per text (mean over every
+ * token of the text, BOS/EOS included, after the final LayerNorm).  Token ids
+ * outside [0, vocab) are clamped on the device.  n_texts = 0 with
+ * n_tokens = 0 is a no-op. */
+tte_status tte_embed(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens,
+                     const int32_t* h_offsets, int32_t n_texts, float* d_out, void* stream);
+
+/* Like tte_embed, but also copies the residual stream after the embedding
+ * LayerNorm and after each of the first n_dump layers into
+ * d_states (fp32 [n_dump + 1, n_tokens, H]).  If n_dump < n_layers the pass
+ * stops there and d_out is not written (it may be NULL). */
+tte_status tte_embed_trace(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens,
+                           const int32_t* h_offsets, int32_t n_texts, float* d_out,
+                           float* d_states, int32_t n_dump, void* stream);
+
+/* Host-only check of a pack against a config, with the same rules and
+ * messages tte_embed applies before enqueuing anything (needs no GPU). */
+tte_status tte_check_pack(const tte_config* cfg, int32_t n_tokens, const int32_t* h_offsets, int32_t n_texts);
+
+/* Free the model (not the borrowed weights or workspace).  Waits for the
+ * model's pending offset upload. */
+tte_status tte_destroy(tte_model* m);
+
+/* Message of the calling thread's last failure ("" if none). */
+const char* tte_last_error(void);
+
+/* ---------------------------------------------------------------------------
+ * Single-kernel entry points (the production kernels on caller buffers),
+ * used by the per-kernel parity tests.  Sizes follow the same rules as the
+ * model's: row widths are multiples of 64, GEMM N and K are multiples of 128.
+ * ------------------------------------------------------------------------- */
+
+typedef enum { TTE_OUT_F32 = 0, TTE_OUT_BF16 = 1, TTE_OUT_I8 = 2 } tte_out_kind;
+
+/* Bias-free LayerNorm of d_x fp32 [rows, width] with gain d_gamma (fp32
+ * [width]; NULL = no normalisation, a plain copy/convert/quantise), written
+ * as fp32, bf16, or 7-bit int8 codes plus one fp32 scale per row into
+ * d_scale (section 何が動くか, encoder paragraph; section 精度と量子化). */
+tte_status tte_op_layernorm(const float* d_x, const float* d_gamma, int32_t rows, int32_t width,
+                            float eps, int32_t out_kind, void* d_out, float* d_scale, void* stream);
+
+/* Per-row 7-bit quantisation of fp32 [rows, width]: amax = max|x|,
+ * q = clamp(rint(x * (63/amax)), -63, 63), scale = amax/63 (zero row: 0, 0),
+ * each step rounded to fp32 (section 精度と量子化). */
+tte_status tte_op_quant7(const float* d_x, int32_t rows, int32_t width, int8_t* d_q, float* d_scale,
+                         void* stream);
+
+typedef enum { TTE_EPI_STORE = 0, TTE_EPI_RESIDUAL = 1, TTE_EPI_GEGLU = 2 } tte_epilogue;
+
+/* Y = A * W^T on the matrix cores.  precision selects the operand format:
+ * TTE_FP32 (A, W fp32), TTE_BF16 (A, W bf16), TTE_INT8 (A int8 codes with
+ * d_a_scale fp32 [M]; W int8 with d_w_scale fp32 [N_w, K/32]; y[m,n] =
+ * a_scale[m] * sum_b w_scale[n,b] * (int32 sum over block b)).
+ * epilogue: STORE writes d_c [M, N] (fp32, or bf16 if out_kind is BF16);
+ * RESIDUAL adds into fp32 d_c [M, N]; GEGLU takes W with 2N rows and writes
+ * d_c[m, n] = GELU(y[m, n]) * y[m, N + n] (erf GELU). */
+tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, const float* d_a_scale,
+                       const void* d_w, const float* d_w_scale, int32_t M, int32_t N, int32_t K,
+                       void* d_c, int32_t out_kind, void* stream);
+
+/* Attention of layer `layer` of model m over the pack described by
+ * h_offsets: d_qkv [n_tokens, 3H] (fp32, or bf16 in TTE_BF16) -> d_o
+ * [n_tokens, H] (same format).  RoPE with positions restarting per text,
+ * text-confined mask, window on local layers (section 何が動くか). */
+tte_status tte_op_attention(tte_model* m, int32_t layer, const void* d_qkv, int32_t n_tokens,
+                            const int32_t* h_offsets, int32_t n_texts, void* d_o, void* stream);
+
+/* Final LayerNorm (gain = the model's final_norm), mean over each text,
+ * L2 normalisation: d_x fp32 [n_tokens, H] -> d_out fp32 [n_texts, H]
+ * (section 何が動くか, pooling paragraph). */
+tte_status tte_op_pool(tte_model* m, const float* d_x, int32_t n_tokens, const int32_t* h_offsets,
+                       int32_t n_texts, float* d_out, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Per-kernel timing with HIP events on the model's stream.
+ * ------------------------------------------------------------------------- */
+
+typedef enum {
+  TTE_K_EMBED = 0, TTE_K_NORM = 1, TTE_K_QUANT = 2, TTE_K_GEMM_QKV = 3, TTE_K_ATTN_GLOBAL = 4,
+  TTE_K_ATTN_LOCAL = 5, TTE_K_GEMM_O = 6, TTE_K_GEMM_GEGLU = 7, TTE_K_GEMM_O2 = 8, TTE_K_POOL = 9,
+  TTE_K_COUNT = 10
+} tte_kernel_class;
+
+/* Start recording an event pair around every launch whose class bit is set
+ * in class_mask, for up to max_launches launches in total. */
+tte_status tte_profile_start(tte_model* m, uint32_t class_mask, int32_t max_launches);
+
+/* Wait for the recorded events and return, per class, the summed kernel
+ * time in milliseconds and the number of timed launches (arrays of
+ * TTE_K_COUNT entries).  Stops recording. */
+tte_status tte_profile_stop(tte_model* m, double* ms_per_class, int64_t* launches_per_class);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TTE_H */

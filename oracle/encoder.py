@@ -41,6 +41,7 @@ import math
 from typing import List, Optional
 
 import numpy as np
+from numpy.lib.stride_tricks import sliding_window_view
 from scipy.special import erf
 
 
@@ -128,6 +129,21 @@ def _softmax_rows(s: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def _window_attention(q: np.ndarray, k: np.ndarray, v: np.ndarray, window: int, scale: float) -> np.ndarray:
+    """One text, one head, local layer: row i attends to keys i-window ..
+    i+window that exist in the text.  Key rows are read through a sliding
+    window view of the zero-padded K and V, so row i holds exactly its own
+    2*window+1 candidate keys; candidates outside the text get -inf."""
+    n, d = q.shape
+    pad = np.zeros((window, d))
+    kw = sliding_window_view(np.concatenate([pad, k, pad]), (2 * window + 1, d))[:, 0]  # [n, 2w+1, d]
+    vw = sliding_window_view(np.concatenate([pad, v, pad]), (2 * window + 1, d))[:, 0]
+    s = np.einsum("nd,nwd->nw", q, kw) * scale
+    j = np.arange(n)[:, None] + np.arange(-window, window + 1)[None, :]
+    s = np.where((j >= 0) & (j < n), s, -np.inf)
+    return np.einsum("nw,nwd->nd", _softmax_rows(s), vw)
+
+
 def attention(qkv: np.ndarray, offsets, n_heads: int, head_dim: int, is_global: bool,
               window: int, rope_base: float) -> np.ndarray:
     """Attention of one layer over a pack.
@@ -152,13 +168,12 @@ def attention(qkv: np.ndarray, offsets, n_heads: int, head_dim: int, is_global: 
     scale = 1.0 / math.sqrt(head_dim)
     for b in range(len(off) - 1):
         lo, hi = off[b], off[b + 1]
-        n = hi - lo
-        i = np.arange(n)
-        allowed = np.ones((n, n), dtype=bool) if is_global else (np.abs(i[:, None] - i[None, :]) <= window)
         for h in range(n_heads):
-            s = (q[lo:hi, h, :] @ k[lo:hi, h, :].T) * scale
-            s = np.where(allowed, s, -np.inf)
-            out[lo:hi, h, :] = _softmax_rows(s) @ v[lo:hi, h, :]
+            qt, kt, vt = q[lo:hi, h, :], k[lo:hi, h, :], v[lo:hi, h, :]
+            if is_global:
+                out[lo:hi, h, :] = _softmax_rows((qt @ kt.T) * scale) @ vt
+            else:
+                out[lo:hi, h, :] = _window_attention(qt, kt, vt, window, scale)
     return out.reshape(T, H)
 
 

@@ -1,0 +1,106 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every function include/tte.h declares, sizes workspaces, and rejects bad
+configs and packs before anything would be enqueued."""
+import ctypes
+import os
+
+import pytest
+
+import tte_inputs as ti
+from conftest import gpu_available
+from transformer_text_embedding_amd import B, make_config
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from transformer_text_embedding_amd.build import build
+        build()
+    return B.lib()
+
+
+def _cfg(name="full_bf16_packs2048", **kw):
+    c = make_config(ti.workload(name)["cfg"], max_tokens=2048, max_text_len=512, max_texts=256)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def test_library_exports_every_declared_function(lib):
+    names = B.header_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+        assert n in B._SIGS, f"{n} has no binding"
+
+
+def test_workspace_size_grows_with_limits(lib):
+    a = B.tte_workspace_size(_cfg())
+    b = B.tte_workspace_size(_cfg(max_tokens=4096))
+    assert 0 < a < b
+    assert a % 256 == 0
+
+
+@pytest.mark.parametrize("field,value", [
+    ("head_dim", 32), ("hidden", 700), ("intermediate", 3000), ("precision", 7), ("max_tokens", 0),
+    ("global_every", 0), ("window", -1), ("ln_eps", 0.0), ("n_layers", 0), ("max_texts", 0)])
+def test_bad_configs_rejected(lib, field, value):
+    c = _cfg(**{field: value})
+    n = ctypes.c_size_t(0)
+    st = lib.tte_workspace_size(ctypes.byref(c), ctypes.byref(n))
+    assert st == B.TTE_E_INVALID
+    assert B.last_error()
+
+
+@pytest.mark.parametrize("T,offsets,ok", [
+    (10, [0, 3, 10], True),
+    (0, [0], True),                 # empty pack: a no-op
+    (10, [1, 3, 10], False),        # offsets[0] != 0
+    (10, [0, 3, 3, 10], False),     # empty text
+    (10, [0, 6, 4, 10], False),     # decreasing
+    (10, [0, 3, 9], False),         # last != n_tokens
+    (3000, [0, 500, 1000, 1500, 2000, 2500, 3000], False),  # n_tokens > max_tokens
+    (600, [0, 600], False),         # text longer than max_text_len
+])
+def test_pack_validation(lib, T, offsets, ok):
+    st = B.tte_check_pack(_cfg(), T, offsets)
+    assert (st == B.TTE_OK) == ok, B.last_error()
+    if not ok:
+        assert st == B.TTE_E_INVALID and B.last_error()
+
+
+def test_too_many_texts(lib):
+    c = _cfg(max_texts=2)
+    assert B.tte_check_pack(c, 6, [0, 2, 4, 6]) == B.TTE_E_INVALID
+    assert "max_texts" in B.last_error()
+
+
+def test_null_model_is_invalid(lib):
+    st = lib.tte_embed(None, None, 0, None, 0, None, None)
+    assert st == B.TTE_E_INVALID
+    assert lib.tte_destroy(None) == B.TTE_E_INVALID
+
+
+def test_op_gemm_shape_checks_need_no_gpu(lib):
+    # N not a multiple of 128 is refused before any launch
+    st = lib.tte_op_gemm(B.TTE_BF16, B.TTE_EPI_STORE, None, None, None, None, 16, 100, 128, None, 0, None)
+    assert st == B.TTE_E_UNSUPPORTED
+    st = lib.tte_op_gemm(B.TTE_BF16, B.TTE_EPI_STORE, None, None, None, None, 16, 128, 96, None, 0, None)
+    assert st == B.TTE_E_UNSUPPORTED
+    st = lib.tte_op_gemm(B.TTE_INT8, B.TTE_EPI_RESIDUAL, None, None, None, None, 16, 128, 128, None, 1, None)
+    assert st == B.TTE_E_INVALID
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device path")
+def test_create_without_device_reports_device_error(lib):
+    cfg = _cfg()
+    layers = (B.tte_layer_weights * cfg.n_layers)()
+    fake = 256
+    for l in range(cfg.n_layers):
+        for f in ("wqkv", "wo", "wi", "wo2", "mlp_norm", "attn_norm"):
+            setattr(layers[l], f, fake)
+    w = B.tte_weights(tok_emb=fake, emb_norm=fake, final_norm=fake, layers=layers)
+    out = ctypes.c_void_p(0)
+    st = lib.tte_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(fake), 1 << 40, ctypes.byref(out))
+    assert st == B.TTE_E_DEVICE
+    assert "device" in B.last_error()

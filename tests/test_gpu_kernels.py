@@ -1,0 +1,281 @@
+"""Per-kernel parity: each production HIP kernel, called through the C ABI on
+seeded inputs, against the oracle's function for the same step.  Sizes span
+several tiles and a ragged tail."""
+import numpy as np
+import pytest
+
+import oracle
+import tte_inputs as ti
+from gpu_util import DEV, dev, empty, host, row_cosines, say, stream, sync, torch
+from transformer_text_embedding_amd import B, Model
+
+pytestmark = pytest.mark.gpu
+
+
+# --------------------------------------------------------------------------
+# LayerNorm / quantisation
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("width", [128, 768, 3072])
+@pytest.mark.parametrize("rows", [1, 357])
+def test_layernorm_fp32_bf16(width, rows):
+    t = torch()
+    rng = np.random.default_rng(100 + width + rows)
+    x = (rng.normal(size=(rows, width)) * 3 + 1).astype(np.float32)
+    g = (1 + rng.normal(0, 0.1, size=width)).astype(np.float32)
+    dx, dg = dev(x), dev(g)
+    out = empty((rows, width), t.float32)
+    outb = empty((rows, width), t.int16)
+    B.tte_op_layernorm(dx.data_ptr(), dg.data_ptr(), rows, width, 1e-5, B.TTE_OUT_F32, out.data_ptr(), 0, stream())
+    B.tte_op_layernorm(dx.data_ptr(), dg.data_ptr(), rows, width, 1e-5, B.TTE_OUT_BF16, outb.data_ptr(), 0, stream())
+    ref = oracle.layer_norm(x, g, 1e-5)
+    np.testing.assert_allclose(host(out), ref, atol=2e-5, rtol=0)
+    got_b = ti.bf16_to_f32(host(outb).view(np.uint16)).astype(np.float64)
+    np.testing.assert_allclose(got_b, ref, rtol=2.0 ** -8, atol=1e-6)
+
+
+@pytest.mark.parametrize("width", [768, 3072])
+def test_quant7_bit_exact(width):
+    t = torch()
+    rng = np.random.default_rng(7 + width)
+    rows = 301
+    x = (rng.normal(size=(rows, width)) * rng.uniform(0.01, 50, size=(rows, 1))).astype(np.float32)
+    x[3] = 0.0
+    x[4, :8] = [63.0, 0.5, 1.5, 2.5, -0.5, -2.5, -63.0, 31.5]
+    x[4, 8:] = 0.25
+    x[5, :] = -1.0
+    dx = dev(x)
+    q = empty((rows, width), t.int8)
+    s = empty((rows,), t.float32)
+    B.tte_op_quant7(dx.data_ptr(), rows, width, q.data_ptr(), s.data_ptr(), stream())
+    qr, sr = oracle.quantize_rows_7bit(x)
+    np.testing.assert_array_equal(host(q), qr)
+    np.testing.assert_array_equal(host(s), sr)
+
+
+def test_layernorm_to_int8_codes():
+    t = torch()
+    rng = np.random.default_rng(5)
+    rows, width = 257, 768
+    x = rng.normal(size=(rows, width)).astype(np.float32)
+    g = np.ones(width, np.float32)
+    dx, dg = dev(x), dev(g)
+    q = empty((rows, width), t.int8)
+    s = empty((rows,), t.float32)
+    B.tte_op_layernorm(dx.data_ptr(), dg.data_ptr(), rows, width, 1e-5, B.TTE_OUT_I8, q.data_ptr(), s.data_ptr(),
+                       stream())
+    qr, sr = oracle.quantize_rows_7bit(oracle.layer_norm(x, g, 1e-5))
+    qg = host(q).astype(np.int64)
+    # the LayerNorm itself is fp32 on the GPU and fp64 in the oracle: a value
+    # within an ulp of a rounding boundary may land on the neighbouring code
+    diff = np.abs(qg - qr)
+    assert diff.max() <= 1 and np.mean(diff) < 1e-3
+    np.testing.assert_allclose(host(s), sr, rtol=1e-5)
+
+
+# --------------------------------------------------------------------------
+# GEMMs
+# --------------------------------------------------------------------------
+
+SHAPES = [(178, 384, 128), (957, 2304, 768), (300, 768, 3072), (130, 512, 256), (1, 128, 128)]
+GEGLU_SHAPES = [(178, 256, 128), (957, 3072, 768), (65, 64, 256)]
+
+
+def _run_gemm(prec, epi, a, a_s, w, w_s, M, N, K, c, out_kind):
+    B.tte_op_gemm(prec, epi, a.data_ptr(), a_s.data_ptr() if a_s is not None else 0, w.data_ptr(),
+                  w_s.data_ptr() if w_s is not None else 0, M, N, K, c.data_ptr(), out_kind, stream())
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_fp32_store_and_residual(M, N, K):
+    t = torch()
+    say(f"gemm fp32 {M}x{N}x{K}")
+    rng = np.random.default_rng(M + N + K)
+    a = rng.normal(size=(M, K)).astype(np.float32)
+    w = rng.normal(0, 0.02, size=(N, K)).astype(np.float32)
+    r = rng.normal(size=(M, N)).astype(np.float32)
+    da, dw = dev(a), dev(w)
+    c = empty((M, N), t.float32)
+    _run_gemm(B.TTE_FP32, B.TTE_EPI_STORE, da, None, dw, None, M, N, K, c, B.TTE_OUT_F32)
+    ref = a.astype(np.float64) @ w.astype(np.float64).T
+    np.testing.assert_allclose(host(c), ref, atol=2e-5, rtol=1e-5)
+    cr = dev(r)
+    _run_gemm(B.TTE_FP32, B.TTE_EPI_RESIDUAL, da, None, dw, None, M, N, K, cr, B.TTE_OUT_F32)
+    np.testing.assert_allclose(host(cr), r + ref, atol=2e-5, rtol=1e-5)
+
+
+@pytest.mark.parametrize("M,N,K", GEGLU_SHAPES)
+@pytest.mark.parametrize("prec", ["fp32", "bf16"])
+def test_gemm_geglu(M, N, K, prec):
+    t = torch()
+    say(f"gemm geglu {prec} {M}x{N}x{K}")
+    rng = np.random.default_rng(11 * M + N + K)
+    a = rng.normal(size=(M, K)).astype(np.float32)
+    w = rng.normal(0, 0.05, size=(2 * N, K)).astype(np.float32)
+    if prec == "bf16":
+        ab, wb = ti.bf16_bits(a), ti.bf16_bits(w)
+        av, wv = ti.bf16_to_f32(ab).astype(np.float64), ti.bf16_to_f32(wb).astype(np.float64)
+        da, dw = dev(ab), dev(wb)
+        p = B.TTE_BF16
+    else:
+        av, wv = a.astype(np.float64), w.astype(np.float64)
+        da, dw = dev(a), dev(w)
+        p = B.TTE_FP32
+    ref = oracle.geglu(av @ wv.T)
+    c = empty((M, N), t.float32)
+    _run_gemm(p, B.TTE_EPI_GEGLU, da, None, dw, None, M, N, K, c, B.TTE_OUT_F32)
+    np.testing.assert_allclose(host(c), ref, atol=5e-5, rtol=1e-4)
+    cb = empty((M, N), t.int16)
+    _run_gemm(p, B.TTE_EPI_GEGLU, da, None, dw, None, M, N, K, cb, B.TTE_OUT_BF16)
+    got = ti.bf16_to_f32(host(cb).view(np.uint16)).astype(np.float64)
+    np.testing.assert_allclose(got, ref, atol=1e-4, rtol=2.0 ** -8)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_bf16(M, N, K):
+    t = torch()
+    say(f"gemm bf16 {M}x{N}x{K}")
+    rng = np.random.default_rng(3 * M + N + K)
+    ab = ti.bf16_bits(rng.normal(size=(M, K)).astype(np.float32))
+    wb = ti.bf16_bits(rng.normal(0, 0.02, size=(N, K)).astype(np.float32))
+    ref = ti.bf16_to_f32(ab).astype(np.float64) @ ti.bf16_to_f32(wb).astype(np.float64).T
+    da, dw = dev(ab), dev(wb)
+    c = empty((M, N), t.float32)
+    _run_gemm(B.TTE_BF16, B.TTE_EPI_STORE, da, None, dw, None, M, N, K, c, B.TTE_OUT_F32)
+    np.testing.assert_allclose(host(c), ref, atol=2e-5, rtol=1e-5)
+    cb = empty((M, N), t.int16)
+    _run_gemm(B.TTE_BF16, B.TTE_EPI_STORE, da, None, dw, None, M, N, K, cb, B.TTE_OUT_BF16)
+    got = ti.bf16_to_f32(host(cb).view(np.uint16)).astype(np.float64)
+    np.testing.assert_allclose(got, ref, atol=1e-6, rtol=2.0 ** -8)
+    r = rng.normal(size=(M, N)).astype(np.float32)
+    cr = dev(r)
+    _run_gemm(B.TTE_BF16, B.TTE_EPI_RESIDUAL, da, None, dw, None, M, N, K, cr, B.TTE_OUT_F32)
+    np.testing.assert_allclose(host(cr), r + ref, atol=2e-5, rtol=1e-5)
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_int8_bit_exact_int32_accumulation(M, N, K):
+    """With every scale 1 the output is the exact integer sum: each 32-block
+    sum is < 2^18 and the running fp32 sum stays below 2^24."""
+    t = torch()
+    say(f"gemm int8 exact {M}x{N}x{K}")
+    rng = np.random.default_rng(5 * M + N + K)
+    wmax = 127 if K <= 1024 else 63
+    qx = rng.integers(-63, 64, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-wmax, wmax + 1, size=(N, K)).astype(np.int8)
+    sx = np.ones(M, np.float32)
+    sw = np.ones((N, K // 32), np.float32)
+    exact = qx.astype(np.int64) @ qw.astype(np.int64).T
+    assert np.abs(exact).max() < 2 ** 24
+    dqx, dsx, dqw, dsw = dev(qx), dev(sx), dev(qw), dev(sw)
+    c = empty((M, N), t.float32)
+    _run_gemm(B.TTE_INT8, B.TTE_EPI_STORE, dqx, dsx, dqw, dsw, M, N, K, c, B.TTE_OUT_F32)
+    got = host(c)
+    assert np.array_equal(got.astype(np.int64), exact) and np.all(got == exact.astype(np.float32))
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+def test_gemm_int8_scaled(M, N, K):
+    t = torch()
+    rng = np.random.default_rng(9 * M + N + K)
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    x[0] = 0.0  # a zero row: scale 0
+    qx, sx = oracle.quantize_rows_7bit(x)
+    qw, sw = ti.quantize_weight_blocks(rng.normal(0, 0.02, size=(N, K)).astype(np.float32))
+    sw[0, 0] = 0.0
+    qw[0, :32] = 0
+    ref = oracle.block_matmul_int8(qx, sx, qw, sw)
+    dqx, dsx, dqw, dsw = dev(qx), dev(sx), dev(qw), dev(sw)
+    c = empty((M, N), t.float32)
+    _run_gemm(B.TTE_INT8, B.TTE_EPI_STORE, dqx, dsx, dqw, dsw, M, N, K, c, B.TTE_OUT_F32)
+    got = host(c)
+    scale = np.abs(ref).max()
+    np.testing.assert_allclose(got, ref, atol=2e-6 * scale, rtol=1e-5)
+    assert np.all(got[0] == 0)
+    # residual and GeGLU epilogues on the same operands
+    r = rng.normal(size=(M, N)).astype(np.float32)
+    cr = dev(r)
+    _run_gemm(B.TTE_INT8, B.TTE_EPI_RESIDUAL, dqx, dsx, dqw, dsw, M, N, K, cr, B.TTE_OUT_F32)
+    np.testing.assert_allclose(host(cr), r + ref, atol=2e-6 * scale + 1e-6, rtol=1e-5)
+    if N % 128 == 0:
+        half = N // 2
+        cg = empty((M, half), t.float32)
+        _run_gemm(B.TTE_INT8, B.TTE_EPI_GEGLU, dqx, dsx, dqw, dsw, M, half, K, cg, B.TTE_OUT_F32)
+        np.testing.assert_allclose(host(cg), oracle.geglu(ref), atol=4e-6 * scale * scale + 1e-6, rtol=1e-4)
+
+
+# --------------------------------------------------------------------------
+# attention
+# --------------------------------------------------------------------------
+
+def _attn_model(precision, hidden, heads):
+    spec = dict(vocab=64, hidden=hidden, heads=heads, head_dim=64, intermediate=2 * hidden, layers=3,
+                precision=precision, global_every=3, window=64, rope_base_global=160000.0,
+                rope_base_local=10000.0, ln_eps=1e-5)
+    cfg = ti.EncoderConfig(name="attn", seed=9, **spec)
+    w = ti.storage_weights(cfg)
+    return Model(spec, w, max_tokens=4096, max_text_len=4096, max_texts=64)
+
+
+ATTN_PACKS = [[8, 40, 130], [1, 64, 65, 200, 3, 129], [957], [2048], [5, 3000, 2]]
+
+
+@pytest.mark.parametrize("lengths", ATTN_PACKS)
+@pytest.mark.parametrize("precision", ["fp32", "bf16"])
+@pytest.mark.parametrize("layer", [0, 1])
+def test_attention(precision, lengths, layer):
+    t = torch()
+    heads = 2 if sum(lengths) > 1000 else 12
+    say(f"attention {precision} layer {layer} lengths {lengths} heads {heads}")
+    m = _attn_model(precision, 64 * heads, heads)
+    rng = np.random.default_rng(sum(lengths) + layer)
+    T, H = sum(lengths), 64 * heads
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    qkv = (rng.normal(size=(T, 3 * H)) * 1.5).astype(np.float32)
+    if precision == "bf16":
+        bits = ti.bf16_bits(qkv)
+        qv = ti.bf16_to_f32(bits).astype(np.float64)
+        dq = dev(bits)
+        o = empty((T, H), t.int16)
+    else:
+        qv = qkv.astype(np.float64)
+        dq = dev(qkv)
+        o = empty((T, H), t.float32)
+    B.tte_op_attention(m.handle, layer, dq.data_ptr(), T, off, o.data_ptr(), stream())
+    is_global = layer % 3 == 0
+    ref = oracle.attention(qv, off, heads, 64, is_global, 64, 160000.0 if is_global else 10000.0)
+    got = host(o)
+    if precision == "bf16":
+        got = ti.bf16_to_f32(got.view(np.uint16)).astype(np.float64)
+        cos = row_cosines(got.reshape(T * heads, 64), ref.reshape(T * heads, 64))
+        assert cos.min() > 0.999, cos.min()
+        # Q, K (after RoPE), V, P and O are rounded to bf16 (relative 2^-9
+        # each); the oracle keeps fp64 after reading the bf16 qkv
+        assert np.abs(got - ref).mean() < 5e-3
+        np.testing.assert_allclose(got, ref, atol=6e-2, rtol=0)
+    else:
+        np.testing.assert_allclose(got, ref, atol=2e-5, rtol=0)
+    m.close()
+
+
+# --------------------------------------------------------------------------
+# pooling
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("lengths", [[8, 40, 130], [1], [33, 32, 31, 1, 64, 100, 2000]])
+def test_pool(lengths):
+    t = torch()
+    spec = ti.workload("tiny_fp32")["cfg"]
+    w = ti.storage_weights(spec)
+    rng = np.random.default_rng(len(lengths))
+    w["final_norm"] = (1 + rng.normal(0, 0.1, size=spec.hidden)).astype(np.float32)
+    m = Model(spec, w, max_tokens=4096, max_text_len=4096, max_texts=16)
+    T = sum(lengths)
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    x = (rng.normal(size=(T, spec.hidden)) * 2 + 0.3).astype(np.float32)
+    dx = dev(x)
+    out = empty((len(lengths), spec.hidden), t.float32)
+    B.tte_op_pool(m.handle, dx.data_ptr(), T, off, out.data_ptr(), stream())
+    ref = oracle.mean_pool_l2(oracle.layer_norm(x, w["final_norm"], 1e-5), off)
+    np.testing.assert_allclose(host(out), ref, atol=2e-6, rtol=0)
+    m.close()

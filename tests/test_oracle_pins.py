@@ -190,13 +190,13 @@ def test_local_equals_global_up_to_65_tokens_and_differs_beyond():
         off = [0, n]
         a = oracle.attention(qkv, off, nh, d, True, 64, 10000.0)
         b = oracle.attention(qkv, off, nh, d, False, 64, 10000.0)
-        np.testing.assert_allclose(a, b, rtol=0, atol=1e-15)
+        np.testing.assert_allclose(a, b, rtol=0, atol=1e-13)
     qkv = rng.normal(size=(66, 3 * nh * d)) * 0.3
     a = oracle.attention(qkv, [0, 66], nh, d, True, 64, 10000.0)
     b = oracle.attention(qkv, [0, 66], nh, d, False, 64, 10000.0)
     # only the first and last rows lose a key at 66 tokens
     diff = np.abs(a - b).max(axis=1)
-    assert diff[0] > 1e-6 and diff[65] > 1e-6 and np.all(diff[1:65] < 1e-15)
+    assert diff[0] > 1e-6 and diff[65] > 1e-6 and np.all(diff[1:65] < 1e-13)
 
 
 def test_attention_packed_equals_alone_and_permutes():

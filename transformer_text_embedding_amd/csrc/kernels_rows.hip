@@ -1,0 +1,351 @@
+// Row-wise kernels: embedding gather + LayerNorm, LayerNorm (fp32 / bf16 /
+// 7-bit int8 output), per-row 7-bit quantisation, final LayerNorm + mean
+// pool + L2.  All are HBM-bound; one wave64 owns one row, holds it in
+// registers (width/64 values per lane, loaded as 16-byte vectors where the
+// width allows) and reduces with cross-lane shuffles, so each row is read
+// once and written once.
+//
+// Bias-free LayerNorm, mean pooling and unit length follow the tensai
+// "テキスト埋め込み" page, section 何が動くか (encoder and pooling
+// paragraphs); the 7-bit row code follows its section 精度と量子化.
+#include "common.h"
+#include "kernels.h"
+
+namespace tte {
+
+template <int EPL>
+struct RowShape {
+  static constexpr int VEC = (EPL % 4 == 0) ? 4 : ((EPL % 2 == 0) ? 2 : 1);
+  static constexpr int CH = EPL / VEC;
+  static constexpr int W = EPL * 64;
+  __device__ static __forceinline__ int col(int c, int lane, int v) { return c * 64 * VEC + lane * VEC + v; }
+};
+
+template <int EPL>
+__device__ __forceinline__ void load_f32_row(const float* __restrict__ row, int lane, float (&v)[EPL]) {
+  using RS = RowShape<EPL>;
+#pragma unroll
+  for (int c = 0; c < RS::CH; ++c) {
+    const float* p = row + RS::col(c, lane, 0);
+    if constexpr (RS::VEC == 4) {
+      float4 t = *reinterpret_cast<const float4*>(p);
+      v[c * 4 + 0] = t.x; v[c * 4 + 1] = t.y; v[c * 4 + 2] = t.z; v[c * 4 + 3] = t.w;
+    } else if constexpr (RS::VEC == 2) {
+      float2 t = *reinterpret_cast<const float2*>(p);
+      v[c * 2 + 0] = t.x; v[c * 2 + 1] = t.y;
+    } else {
+      v[c] = p[0];
+    }
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void store_f32_row(float* __restrict__ row, int lane, const float (&v)[EPL]) {
+  using RS = RowShape<EPL>;
+#pragma unroll
+  for (int c = 0; c < RS::CH; ++c) {
+    float* p = row + RS::col(c, lane, 0);
+    if constexpr (RS::VEC == 4) {
+      *reinterpret_cast<float4*>(p) = make_float4(v[c * 4 + 0], v[c * 4 + 1], v[c * 4 + 2], v[c * 4 + 3]);
+    } else if constexpr (RS::VEC == 2) {
+      *reinterpret_cast<float2*>(p) = make_float2(v[c * 2 + 0], v[c * 2 + 1]);
+    } else {
+      p[0] = v[c];
+    }
+  }
+}
+
+template <int EPL>
+__device__ __forceinline__ void store_bf16_row(uint16_t* __restrict__ row, int lane, const float (&v)[EPL]) {
+  using RS = RowShape<EPL>;
+#pragma unroll
+  for (int c = 0; c < RS::CH; ++c) {
+    uint16_t* p = row + RS::col(c, lane, 0);
+    if constexpr (RS::VEC == 4) {
+      u16x4 t = {f32_to_bf16(v[c * 4 + 0]), f32_to_bf16(v[c * 4 + 1]), f32_to_bf16(v[c * 4 + 2]),
+                 f32_to_bf16(v[c * 4 + 3])};
+      *reinterpret_cast<u16x4*>(p) = t;
+    } else {
+#pragma unroll
+      for (int e = 0; e < RS::VEC; ++e) p[e] = f32_to_bf16(v[c * RS::VEC + e]);
+    }
+  }
+}
+
+// 7-bit codes of a row held in registers; returns the row scale amax/63.
+template <int EPL>
+__device__ __forceinline__ float store_q7_row(int8_t* __restrict__ row, int lane, const float (&v)[EPL]) {
+  using RS = RowShape<EPL>;
+  float amax = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) amax = fmaxf(amax, fabsf(v[i]));
+  amax = wave_max(amax);
+  const float inv = amax > 0.f ? 63.f / amax : 0.f;
+#pragma unroll
+  for (int c = 0; c < RS::CH; ++c) {
+    int8_t* p = row + RS::col(c, lane, 0);
+    if constexpr (RS::VEC == 4) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) packed |= ((uint32_t)(uint8_t)(int8_t)quant7(v[c * 4 + e], inv)) << (8 * e);
+      *reinterpret_cast<uint32_t*>(p) = packed;
+    } else {
+#pragma unroll
+      for (int e = 0; e < RS::VEC; ++e) p[e] = (int8_t)quant7(v[c * RS::VEC + e], inv);
+    }
+  }
+  return amax > 0.f ? amax / 63.f : 0.f;
+}
+
+// In-register bias-free LayerNorm of one row: two passes over registers
+// (mean, then centred sum of squares), fp32 statistics.
+template <int EPL>
+__device__ __forceinline__ void layernorm_regs(float (&v)[EPL], const float* __restrict__ gamma, int lane,
+                                               float eps) {
+  using RS = RowShape<EPL>;
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) s += v[i];
+  const float mean = wave_sum(s) * (1.f / RS::W);
+  float q = 0.f;
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) {
+    v[i] -= mean;
+    q += v[i] * v[i];
+  }
+  const float rstd = 1.f / sqrtf(wave_sum(q) * (1.f / RS::W) + eps);
+  float g[EPL];
+  load_f32_row<EPL>(gamma, lane, g);
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) v[i] = v[i] * rstd * g[i];
+}
+
+// --------------------------------------------------------------------------
+// embedding gather + LayerNorm; per-token text bounds
+// --------------------------------------------------------------------------
+
+template <int EPL, int PREC>
+__global__ __launch_bounds__(256) void k_embed_ln(const int32_t* __restrict__ ids, int T,
+                                                  const void* __restrict__ table,
+                                                  const float* __restrict__ table_scale, int vocab,
+                                                  const float* __restrict__ gamma, float eps,
+                                                  const int* __restrict__ off, int n_texts,
+                                                  float* __restrict__ x, Seg* __restrict__ seg) {
+  using RS = RowShape<EPL>;
+  constexpr int H = RS::W;
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  int id = ids[t];
+  id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+  float v[EPL];
+  if constexpr (PREC == P_F32) {
+    load_f32_row<EPL>(reinterpret_cast<const float*>(table) + (size_t)id * H, lane, v);
+  } else if constexpr (PREC == P_BF16) {
+    const uint16_t* r = reinterpret_cast<const uint16_t*>(table) + (size_t)id * H;
+#pragma unroll
+    for (int c = 0; c < RS::CH; ++c)
+#pragma unroll
+      for (int e = 0; e < RS::VEC; ++e) v[c * RS::VEC + e] = bf16_to_f32(r[RS::col(c, lane, e)]);
+  } else {
+    const int8_t* r = reinterpret_cast<const int8_t*>(table) + (size_t)id * H;
+    const float* sc = table_scale + (size_t)id * (H / 32);
+#pragma unroll
+    for (int c = 0; c < RS::CH; ++c)
+#pragma unroll
+      for (int e = 0; e < RS::VEC; ++e) {
+        const int k = RS::col(c, lane, e);
+        v[c * RS::VEC + e] = (float)r[k] * sc[k >> 5];
+      }
+  }
+  layernorm_regs<EPL>(v, gamma, lane, eps);
+  store_f32_row<EPL>(x + (size_t)t * H, lane, v);
+  if (lane == 0) {
+    // largest b with off[b] <= t (off is strictly increasing, off[0] = 0)
+    int lo = 0, hi = n_texts;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (off[mid] <= t) lo = mid; else hi = mid;
+    }
+    seg[t] = Seg{off[lo], off[lo + 1]};
+  }
+}
+
+// --------------------------------------------------------------------------
+// LayerNorm / conversion / quantisation of fp32 rows
+// --------------------------------------------------------------------------
+
+template <int EPL, int OUT, bool NORM>
+__global__ __launch_bounds__(256) void k_ln(const float* __restrict__ x, const float* __restrict__ gamma, int rows,
+                                            float eps, void* __restrict__ out, float* __restrict__ out_scale) {
+  using RS = RowShape<EPL>;
+  constexpr int Wd = RS::W;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float v[EPL];
+  load_f32_row<EPL>(x + (size_t)r * Wd, lane, v);
+  if constexpr (NORM) layernorm_regs<EPL>(v, gamma, lane, eps);
+  if constexpr (OUT == O_F32) {
+    store_f32_row<EPL>(reinterpret_cast<float*>(out) + (size_t)r * Wd, lane, v);
+  } else if constexpr (OUT == O_BF16) {
+    store_bf16_row<EPL>(reinterpret_cast<uint16_t*>(out) + (size_t)r * Wd, lane, v);
+  } else {
+    const float s = store_q7_row<EPL>(reinterpret_cast<int8_t*>(out) + (size_t)r * Wd, lane, v);
+    if (lane == 0) out_scale[r] = s;
+  }
+}
+
+// --------------------------------------------------------------------------
+// final LayerNorm + mean pool + L2 normalisation
+// --------------------------------------------------------------------------
+
+// Stage 1: one block per unit (up to POOL_ROWS rows of one text): LayerNorm
+// of each row in registers, per-wave column sums, then a fixed-order sum of
+// the 4 waves through LDS -> partial[u, :].  No atomics: deterministic.
+template <int EPL>
+__global__ __launch_bounds__(256) void k_pool_partial(const float* __restrict__ x, const float* __restrict__ gamma,
+                                                      float eps, const int* __restrict__ off,
+                                                      const int* __restrict__ unit_start, int n_texts,
+                                                      float* __restrict__ partial) {
+  using RS = RowShape<EPL>;
+  constexpr int H = RS::W;
+  __shared__ float red[4][H];
+  const int u = blockIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int lo = 0, hi = n_texts;  // text b with unit_start[b] <= u < unit_start[b+1]
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (unit_start[mid] <= u) lo = mid; else hi = mid;
+  }
+  const int r0 = off[lo] + (u - unit_start[lo]) * POOL_ROWS;
+  const int r1 = min(r0 + POOL_ROWS, off[lo + 1]);
+  float acc[EPL];
+#pragma unroll
+  for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
+  for (int r = r0 + w; r < r1; r += 4) {
+    float v[EPL];
+    load_f32_row<EPL>(x + (size_t)r * H, lane, v);
+    layernorm_regs<EPL>(v, gamma, lane, eps);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) acc[i] += v[i];
+  }
+#pragma unroll
+  for (int c = 0; c < RS::CH; ++c)
+#pragma unroll
+    for (int e = 0; e < RS::VEC; ++e) red[w][RS::col(c, lane, e)] = acc[c * RS::VEC + e];
+  __syncthreads();
+  for (int j = threadIdx.x; j < H; j += 256)
+    partial[(size_t)u * H + j] = ((red[0][j] + red[1][j]) + red[2][j]) + red[3][j];
+}
+
+// Stage 2: one block per text: sum its units in order, divide by the token
+// count, divide by max(||e||, 1e-12).
+template <int H>
+__global__ __launch_bounds__(256) void k_pool_finish(const float* __restrict__ partial, const int* __restrict__ off,
+                                                     const int* __restrict__ unit_start, float* __restrict__ out) {
+  constexpr int PER = (H + 255) / 256;
+  __shared__ float red[4];
+  const int b = blockIdx.x;
+  const int u0 = unit_start[b], u1 = unit_start[b + 1];
+  const float inv_n = 1.f / (float)(off[b + 1] - off[b]);
+  float e[PER];
+  float ss = 0.f;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    float s = 0.f;
+    if (j < H)
+      for (int u = u0; u < u1; ++u) s += partial[(size_t)u * H + j];
+    e[i] = s * inv_n;
+    ss += (j < H) ? e[i] * e[i] : 0.f;
+  }
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float norm = sqrtf(((red[0] + red[1]) + red[2]) + red[3]);
+  const float inv = 1.f / fmaxf(norm, 1e-12f);
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int j = threadIdx.x + 256 * i;
+    if (j < H) out[(size_t)b * H + j] = e[i] * inv;
+  }
+}
+
+// --------------------------------------------------------------------------
+// launchers
+// --------------------------------------------------------------------------
+
+bool row_width_supported(int width) {
+  if (width <= 0 || width % 64 != 0) return false;
+  switch (width / 64) {
+    case 2: case 4: case 8: case 12: case 16: case 24: case 32: case 48: case 64: return true;
+    default: return false;
+  }
+}
+
+#define TTE_EPL_DISPATCH(width, MACRO) \
+  switch ((width) / 64) {              \
+    case 2: MACRO(2); break;           \
+    case 4: MACRO(4); break;           \
+    case 8: MACRO(8); break;           \
+    case 12: MACRO(12); break;         \
+    case 16: MACRO(16); break;         \
+    case 24: MACRO(24); break;         \
+    case 32: MACRO(32); break;         \
+    case 48: MACRO(48); break;         \
+    case 64: MACRO(64); break;         \
+    default: break;                    \
+  }
+
+void launch_embed_ln(int prec, const int32_t* ids, int T, const void* table, const float* table_scale, int vocab,
+                     const float* gamma, float eps, int H, const int* d_off, int n_texts, float* x, Seg* seg,
+                     hipStream_t s) {
+  if (T <= 0) return;
+  const dim3 grid((T + 3) / 4), block(256);
+#define L_EMB(E)                                                                                                    \
+  if (prec == P_F32)                                                                                                \
+    k_embed_ln<E, P_F32><<<grid, block, 0, s>>>(ids, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x,   \
+                                                 seg);                                                              \
+  else if (prec == P_BF16)                                                                                          \
+    k_embed_ln<E, P_BF16><<<grid, block, 0, s>>>(ids, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x,  \
+                                                  seg);                                                             \
+  else                                                                                                              \
+    k_embed_ln<E, P_I8><<<grid, block, 0, s>>>(ids, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x, seg);
+  TTE_EPL_DISPATCH(H, L_EMB)
+#undef L_EMB
+}
+
+void launch_ln(const float* x, const float* gamma, int rows, int width, float eps, int out_kind, void* out,
+               float* out_scale, hipStream_t s) {
+  if (rows <= 0) return;
+  const dim3 grid((rows + 3) / 4), block(256);
+#define L_LN(E)                                                                                        \
+  if (gamma) {                                                                                         \
+    if (out_kind == O_F32) k_ln<E, O_F32, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale);   \
+    else if (out_kind == O_BF16) k_ln<E, O_BF16, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale); \
+    else k_ln<E, O_I8, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale);              \
+  } else {                                                                                             \
+    if (out_kind == O_F32) k_ln<E, O_F32, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale);  \
+    else if (out_kind == O_BF16) k_ln<E, O_BF16, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale); \
+    else k_ln<E, O_I8, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale);             \
+  }
+  TTE_EPL_DISPATCH(width, L_LN)
+#undef L_LN
+}
+
+void launch_quant7(const float* x, int rows, int width, int8_t* q, float* scale, hipStream_t s) {
+  launch_ln(x, nullptr, rows, width, 0.f, O_I8, q, scale, s);
+}
+
+void launch_pool(const float* x, const float* gamma, float eps, int H, const int* d_off, const int* d_unit,
+                 int n_texts, int n_units, float* partial, float* out, hipStream_t s) {
+  if (n_texts <= 0) return;
+#define L_POOL(E)                                                                                          \
+  k_pool_partial<E><<<n_units, 256, 0, s>>>(x, gamma, eps, d_off, d_unit, n_texts, partial);               \
+  k_pool_finish<E * 64><<<n_texts, 256, 0, s>>>(partial, d_off, d_unit, out);
+  TTE_EPL_DISPATCH(H, L_POOL)
+#undef L_POOL
+}
+
+}  // namespace tte

@@ -1,0 +1,547 @@
+// C ABI and engine: configuration checks, workspace carve-up, RoPE tables,
+// host-side validation of packs, and the per-layer launch sequence of the
+// packed embedding pass (tensai "テキスト埋め込み" page, section 何が動くか:
+// embedding, 25 pre-norm layers of attention + GeGLU with the global/local
+// schedule, mean pooling and unit length).
+//
+// Layer structure (the ModernBERT layout the page names): embedding
+// LayerNorm; per layer, x += Wo * attn(Wqkv * norm_attn(x)) with no norm on
+// layer 0, then x += Wo2 * GeGLU(Wi * norm_mlp(x)); final LayerNorm; mean
+// over each text; L2 normalisation.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "tte.h"
+
+using namespace tte;
+
+namespace {
+
+thread_local std::string g_err;
+
+tte_status fail(tte_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+size_t al(size_t v) { return (v + 255) & ~size_t(255); }
+
+struct Layout {
+  size_t x, xa, ascale, qkv, o, y, seg, off, unit, partial, cosg, sing, cosl, sinl, total;
+  int max_units;
+};
+
+int act_bytes(int prec) { return prec == TTE_BF16 ? 2 : 4; }
+
+Layout layout_of(const tte_config& c) {
+  Layout L{};
+  const size_t T = (size_t)c.max_tokens, H = (size_t)c.hidden, I = (size_t)c.intermediate;
+  const size_t ab = (size_t)act_bytes(c.precision);
+  L.max_units = c.max_tokens / POOL_ROWS + c.max_texts + 1;
+  size_t p = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = p;
+    p += al(bytes);
+    return at;
+  };
+  L.x = take(T * H * 4);
+  L.xa = take(c.precision == TTE_INT8 ? T * (H > I ? H : I) : T * H * ab);
+  L.ascale = take(T * 4);
+  L.qkv = take(T * 3 * H * ab);
+  L.o = take(T * H * ab);
+  L.y = take(T * I * ab);
+  L.seg = take(T * sizeof(Seg));
+  L.off = take(((size_t)c.max_texts + 1) * 4);
+  L.unit = take(((size_t)c.max_texts + 1) * 4);
+  L.partial = take((size_t)L.max_units * H * 4);
+  const size_t rope = (size_t)c.max_text_len * 32 * 4;
+  L.cosg = take(rope);
+  L.sing = take(rope);
+  L.cosl = take(rope);
+  L.sinl = take(rope);
+  L.total = p;
+  return L;
+}
+
+bool check_config(const tte_config* c, std::string* why) {
+  auto bad = [&](const char* m) {
+    *why = m;
+    return false;
+  };
+  if (!c) return bad("config is NULL");
+  if (c->precision < TTE_FP32 || c->precision > TTE_INT8) return bad("precision must be TTE_FP32, TTE_BF16 or TTE_INT8");
+  if (c->vocab <= 0 || c->n_layers <= 0 || c->n_heads <= 0) return bad("vocab, n_layers and n_heads must be positive");
+  if (c->head_dim != 64) return bad("head_dim must be 64");
+  if (c->hidden != c->n_heads * c->head_dim) return bad("hidden must equal n_heads * head_dim");
+  if (c->hidden % 128 != 0 || !row_width_supported(c->hidden))
+    return bad("hidden must be a multiple of 128 with hidden/64 in {2,4,8,12,16,24,32,48,64}");
+  if (c->intermediate <= 0 || c->intermediate % 128 != 0 || !row_width_supported(c->intermediate))
+    return bad("intermediate must be a multiple of 128 with intermediate/64 in {2,4,8,12,16,24,32,48,64}");
+  if (c->global_every <= 0) return bad("global_every must be positive");
+  if (c->window < 0) return bad("window must be >= 0");
+  if (!(c->ln_eps > 0.f)) return bad("ln_eps must be > 0");
+  if (!(c->rope_base_global > 0.f) || !(c->rope_base_local > 0.f)) return bad("RoPE bases must be > 0");
+  if (c->max_tokens <= 0 || c->max_text_len <= 0 || c->max_texts <= 0)
+    return bad("max_tokens, max_text_len and max_texts must be positive");
+  if (c->max_tokens > (1 << 24)) return bad("max_tokens above 2^24");
+  return true;
+}
+
+tte_status check_pack(const tte_config& c, int32_t n_tokens, const int32_t* h_off, int32_t n_texts) {
+  if (n_texts < 0 || n_tokens < 0) return fail(TTE_E_INVALID, "n_texts and n_tokens must be >= 0");
+  if (n_texts == 0) {
+    if (n_tokens != 0) return fail(TTE_E_INVALID, "n_tokens must be 0 when n_texts is 0");
+    return TTE_OK;
+  }
+  if (!h_off) return fail(TTE_E_INVALID, "h_offsets is NULL");
+  if (n_texts > c.max_texts) return fail(TTE_E_INVALID, "n_texts exceeds max_texts");
+  if (n_tokens > c.max_tokens) return fail(TTE_E_INVALID, "n_tokens exceeds max_tokens");
+  if (h_off[0] != 0) return fail(TTE_E_INVALID, "offsets[0] must be 0");
+  for (int b = 0; b < n_texts; ++b) {
+    const int64_t len = (int64_t)h_off[b + 1] - h_off[b];
+    if (len <= 0) return fail(TTE_E_INVALID, "offsets must be strictly increasing (empty text at " + std::to_string(b) + ")");
+    if (len > c.max_text_len) return fail(TTE_E_INVALID, "text " + std::to_string(b) + " is longer than max_text_len");
+  }
+  if (h_off[n_texts] != n_tokens) return fail(TTE_E_INVALID, "offsets[n_texts] must equal n_tokens");
+  return TTE_OK;
+}
+
+}  // namespace
+
+struct tte_model {
+  tte_config cfg;
+  tte_weights w;
+  std::vector<tte_layer_weights> layers;
+  Layout L;
+  uint8_t* ws;
+  int device;
+  // carved workspace
+  float* x;
+  void* xa;
+  float* ascale;
+  void* qkv;
+  void* o;
+  void* y;
+  Seg* seg;
+  int* d_off;
+  int* d_unit;
+  float* partial;
+  const float *cosg, *sing, *cosl, *sinl;
+  // pinned staging for the per-call offsets upload
+  int* h_stage;
+  hipEvent_t stage_ev;
+  bool stage_pending;
+  // profiling
+  bool prof_on;
+  uint32_t prof_mask;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> ev_cls;
+  int ev_used;
+  bool ev_overflow;
+};
+
+namespace {
+
+struct ProfScope {
+  tte_model* m;
+  hipStream_t s;
+  int idx;
+  ProfScope(tte_model* m_, int cls, hipStream_t s_) : m(m_), s(s_), idx(-1) {
+    if (!m->prof_on || !(m->prof_mask & (1u << cls))) return;
+    if (2 * (m->ev_used + 1) > (int)m->ev.size()) {
+      m->ev_overflow = true;
+      return;
+    }
+    idx = m->ev_used++;
+    m->ev_cls[idx] = cls;
+    hipEventRecord(m->ev[2 * idx], s);
+  }
+  ~ProfScope() {
+    if (idx >= 0) hipEventRecord(m->ev[2 * idx + 1], s);
+  }
+};
+
+tte_status hip_check(hipError_t e, const char* what) {
+  if (e == hipSuccess) return TTE_OK;
+  return fail(TTE_E_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// Copies offsets and pool-unit starts into the workspace (stream-ordered,
+// from pinned staging that is reused only once the previous copy is done).
+tte_status upload_pack(tte_model* m, const int32_t* h_off, int n_texts, int* n_units, hipStream_t s) {
+  if (m->stage_pending) {
+    tte_status st = hip_check(hipEventSynchronize(m->stage_ev), "hipEventSynchronize");
+    if (st != TTE_OK) return st;
+    m->stage_pending = false;
+  }
+  int* so = m->h_stage;
+  int* su = m->h_stage + (m->cfg.max_texts + 1);
+  std::memcpy(so, h_off, sizeof(int) * (size_t)(n_texts + 1));
+  su[0] = 0;
+  for (int b = 0; b < n_texts; ++b) su[b + 1] = su[b] + (h_off[b + 1] - h_off[b] + POOL_ROWS - 1) / POOL_ROWS;
+  *n_units = su[n_texts];
+  tte_status st = hip_check(hipMemcpyAsync(m->d_off, so, sizeof(int) * (n_texts + 1), hipMemcpyHostToDevice, s),
+                            "hipMemcpyAsync(offsets)");
+  if (st != TTE_OK) return st;
+  st = hip_check(hipMemcpyAsync(m->d_unit, su, sizeof(int) * (n_texts + 1), hipMemcpyHostToDevice, s),
+                 "hipMemcpyAsync(units)");
+  if (st != TTE_OK) return st;
+  st = hip_check(hipEventRecord(m->stage_ev, s), "hipEventRecord");
+  if (st != TTE_OK) return st;
+  m->stage_pending = true;
+  return TTE_OK;
+}
+
+// Per-token text bounds from the device offsets (used by the attention
+// entry point; the full pass gets them from the embedding kernel).
+__global__ void k_seg(const int* __restrict__ off, int n_texts, int T, Seg* __restrict__ seg) {
+  const int t = blockIdx.x * blockDim.x + threadIdx.x;
+  if (t >= T) return;
+  int lo = 0, hi = n_texts;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (off[mid] <= t) lo = mid; else hi = mid;
+  }
+  seg[t] = Seg{off[lo], off[lo + 1]};
+}
+
+tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t* h_off, int32_t B, float* d_out,
+                    float* d_states, int32_t n_dump, void* stream) {
+  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+  const tte_config& c = m->cfg;
+  tte_status st = check_pack(c, T, h_off, B);
+  if (st != TTE_OK) return st;
+  if (B == 0) return TTE_OK;
+  if (!d_ids) return fail(TTE_E_INVALID, "d_token_ids is NULL");
+  if (d_states) {
+    if (n_dump < 0 || n_dump > c.n_layers) return fail(TTE_E_INVALID, "n_dump must be in [0, n_layers]");
+  } else {
+    n_dump = -1;
+  }
+  const int n_run = (d_states && n_dump < c.n_layers) ? n_dump : c.n_layers;
+  if (n_run == c.n_layers && !d_out) return fail(TTE_E_INVALID, "d_out is NULL");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = hip_check(hipSetDevice(m->device), "hipSetDevice");
+  if (st != TTE_OK) return st;
+  (void)hipGetLastError();
+  int n_units = 0;
+  st = upload_pack(m, h_off, B, &n_units, s);
+  if (st != TTE_OK) return st;
+
+  const int P = c.precision, H = c.hidden, I = c.intermediate, nh = c.n_heads;
+  const int act = P == TTE_BF16 ? O_BF16 : O_F32;  // format of qkv / o / y
+  const size_t state_bytes = (size_t)T * H * 4;
+  {
+    ProfScope ps(m, TTE_K_EMBED, s);
+    launch_embed_ln(P, d_ids, T, m->w.tok_emb, m->w.tok_emb_scale, c.vocab, m->w.emb_norm, c.ln_eps, H, m->d_off, B,
+                    m->x, m->seg, s);
+  }
+  if (d_states) hipMemcpyAsync(d_states, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
+
+  for (int l = 0; l < n_run; ++l) {
+    const tte_layer_weights& LW = m->layers[l];
+    const int glob = (l % c.global_every) == 0;
+    // attention sub-layer input: no norm on layer 0
+    const void* a_in = m->xa;
+    if (P == TTE_FP32 && l == 0) {
+      a_in = m->x;
+    } else {
+      ProfScope ps(m, P == TTE_INT8 && l == 0 ? TTE_K_QUANT : TTE_K_NORM, s);
+      launch_ln(m->x, l == 0 ? nullptr : LW.attn_norm, T, H, c.ln_eps, P == TTE_INT8 ? O_I8 : act, m->xa, m->ascale, s);
+    }
+    {
+      ProfScope ps(m, TTE_K_GEMM_QKV, s);
+      launch_gemm(P, E_STORE, a_in, m->ascale, LW.wqkv, LW.wqkv_scale, T, 3 * H, H, m->qkv, act, s);
+    }
+    {
+      ProfScope ps(m, glob ? TTE_K_ATTN_GLOBAL : TTE_K_ATTN_LOCAL, s);
+      launch_attention(P == TTE_BF16 ? P_BF16 : P_F32, m->qkv, m->o, m->seg, glob ? m->cosg : m->cosl,
+                       glob ? m->sing : m->sinl, T, nh, glob, c.window, s);
+    }
+    const void* o_in = m->o;
+    if (P == TTE_INT8) {
+      ProfScope ps(m, TTE_K_QUANT, s);
+      launch_quant7(reinterpret_cast<const float*>(m->o), T, H, reinterpret_cast<int8_t*>(m->xa), m->ascale, s);
+      o_in = m->xa;
+    }
+    {
+      ProfScope ps(m, TTE_K_GEMM_O, s);
+      launch_gemm(P, E_RESID, o_in, m->ascale, LW.wo, LW.wo_scale, T, H, H, m->x, O_F32, s);
+    }
+    {
+      ProfScope ps(m, TTE_K_NORM, s);
+      launch_ln(m->x, LW.mlp_norm, T, H, c.ln_eps, P == TTE_INT8 ? O_I8 : act, m->xa, m->ascale, s);
+    }
+    {
+      ProfScope ps(m, TTE_K_GEMM_GEGLU, s);
+      launch_gemm(P, E_GEGLU, m->xa, m->ascale, LW.wi, LW.wi_scale, T, I, H, m->y, act, s);
+    }
+    const void* y_in = m->y;
+    if (P == TTE_INT8) {
+      ProfScope ps(m, TTE_K_QUANT, s);
+      launch_quant7(reinterpret_cast<const float*>(m->y), T, I, reinterpret_cast<int8_t*>(m->xa), m->ascale, s);
+      y_in = m->xa;
+    }
+    {
+      ProfScope ps(m, TTE_K_GEMM_O2, s);
+      launch_gemm(P, E_RESID, y_in, m->ascale, LW.wo2, LW.wo2_scale, T, H, I, m->x, O_F32, s);
+    }
+    if (d_states) hipMemcpyAsync(d_states + (size_t)(l + 1) * T * H, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
+  }
+  if (n_run == c.n_layers) {
+    ProfScope ps(m, TTE_K_POOL, s);
+    launch_pool(m->x, m->w.final_norm, c.ln_eps, H, m->d_off, m->d_unit, B, n_units, m->partial, d_out, s);
+  }
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* tte_last_error(void) { return g_err.c_str(); }
+
+tte_status tte_workspace_size(const tte_config* cfg, size_t* bytes) {
+  std::string why;
+  if (!check_config(cfg, &why)) return fail(TTE_E_INVALID, why);
+  if (!bytes) return fail(TTE_E_INVALID, "bytes is NULL");
+  *bytes = layout_of(*cfg).total;
+  return TTE_OK;
+}
+
+tte_status tte_check_pack(const tte_config* cfg, int32_t n_tokens, const int32_t* h_offsets, int32_t n_texts) {
+  std::string why;
+  if (!check_config(cfg, &why)) return fail(TTE_E_INVALID, why);
+  return check_pack(*cfg, n_tokens, h_offsets, n_texts);
+}
+
+tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_workspace, size_t workspace_bytes,
+                      tte_model** out) {
+  std::string why;
+  if (!check_config(cfg, &why)) return fail(TTE_E_INVALID, why);
+  if (!w || !out) return fail(TTE_E_INVALID, "weights or out is NULL");
+  *out = nullptr;
+  const tte_config& c = *cfg;
+  const bool q = c.precision == TTE_INT8;
+  if (!w->tok_emb || !w->emb_norm || !w->final_norm || !w->layers || (q && !w->tok_emb_scale))
+    return fail(TTE_E_INVALID, "a required weight pointer is NULL");
+  for (int l = 0; l < c.n_layers; ++l) {
+    const tte_layer_weights& L = w->layers[l];
+    if (!L.wqkv || !L.wo || !L.wi || !L.wo2 || !L.mlp_norm || (l > 0 && !L.attn_norm))
+      return fail(TTE_E_INVALID, "layer " + std::to_string(l) + ": a required weight pointer is NULL");
+    if (q && (!L.wqkv_scale || !L.wo_scale || !L.wi_scale || !L.wo2_scale))
+      return fail(TTE_E_INVALID, "layer " + std::to_string(l) + ": an int8 scale pointer is NULL");
+  }
+  int ndev = 0;
+  if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
+    (void)hipGetLastError();
+    return fail(TTE_E_DEVICE, "no HIP device present");
+  }
+  const Layout L = layout_of(c);
+  if (!d_workspace) return fail(TTE_E_INVALID, "d_workspace is NULL");
+  if (((uintptr_t)d_workspace & 255u) != 0) return fail(TTE_E_INVALID, "d_workspace must be 256-byte aligned");
+  if (workspace_bytes < L.total) return fail(TTE_E_NOMEM, "workspace smaller than tte_workspace_size");
+
+  tte_model* m = new (std::nothrow) tte_model();
+  if (!m) return fail(TTE_E_NOMEM, "host allocation failed");
+  m->cfg = c;
+  m->w = *w;
+  m->layers.assign(w->layers, w->layers + c.n_layers);
+  m->w.layers = m->layers.data();
+  m->L = L;
+  m->ws = reinterpret_cast<uint8_t*>(d_workspace);
+  hipGetDevice(&m->device);
+  uint8_t* b = m->ws;
+  m->x = reinterpret_cast<float*>(b + L.x);
+  m->xa = b + L.xa;
+  m->ascale = reinterpret_cast<float*>(b + L.ascale);
+  m->qkv = b + L.qkv;
+  m->o = b + L.o;
+  m->y = b + L.y;
+  m->seg = reinterpret_cast<Seg*>(b + L.seg);
+  m->d_off = reinterpret_cast<int*>(b + L.off);
+  m->d_unit = reinterpret_cast<int*>(b + L.unit);
+  m->partial = reinterpret_cast<float*>(b + L.partial);
+  m->cosg = reinterpret_cast<const float*>(b + L.cosg);
+  m->sing = reinterpret_cast<const float*>(b + L.sing);
+  m->cosl = reinterpret_cast<const float*>(b + L.cosl);
+  m->sinl = reinterpret_cast<const float*>(b + L.sinl);
+
+  // RoPE tables: angle p * base^(-2c/64), rotate-half pairs (c, c + 32),
+  // evaluated in double and rounded to fp32.
+  const size_t n = (size_t)c.max_text_len * 32;
+  std::vector<float> tab(4 * n);
+  const double bases[2] = {c.rope_base_global, c.rope_base_local};
+  for (int which = 0; which < 2; ++which)
+    for (int p = 0; p < c.max_text_len; ++p)
+      for (int k = 0; k < 32; ++k) {
+        const double ang = (double)p * std::pow(bases[which], -2.0 * k / 64.0);
+        tab[(2 * which) * n + (size_t)p * 32 + k] = (float)std::cos(ang);
+        tab[(2 * which + 1) * n + (size_t)p * 32 + k] = (float)std::sin(ang);
+      }
+  tte_status st = TTE_OK;
+  const size_t dst[4] = {L.cosg, L.sing, L.cosl, L.sinl};
+  for (int i = 0; i < 4 && st == TTE_OK; ++i)
+    st = hip_check(hipMemcpy(b + dst[i], tab.data() + i * n, n * 4, hipMemcpyHostToDevice), "hipMemcpy(rope)");
+  if (st == TTE_OK)
+    st = hip_check(hipHostMalloc((void**)&m->h_stage, sizeof(int) * 2 * ((size_t)c.max_texts + 1), hipHostMallocDefault),
+                   "hipHostMalloc");
+  if (st == TTE_OK) st = hip_check(hipEventCreateWithFlags(&m->stage_ev, hipEventDisableTiming), "hipEventCreate");
+  if (st != TTE_OK) {
+    if (m->h_stage) hipHostFree(m->h_stage);
+    delete m;
+    return st;
+  }
+  *out = m;
+  return TTE_OK;
+}
+
+tte_status tte_embed(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens, const int32_t* h_offsets,
+                     int32_t n_texts, float* d_out, void* stream) {
+  return run_pass(m, d_token_ids, n_tokens, h_offsets, n_texts, d_out, nullptr, 0, stream);
+}
+
+tte_status tte_embed_trace(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens, const int32_t* h_offsets,
+                           int32_t n_texts, float* d_out, float* d_states, int32_t n_dump, void* stream) {
+  if (!d_states) return fail(TTE_E_INVALID, "d_states is NULL");
+  return run_pass(m, d_token_ids, n_tokens, h_offsets, n_texts, d_out, d_states, n_dump, stream);
+}
+
+tte_status tte_destroy(tte_model* m) {
+  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+  if (m->stage_pending) hipEventSynchronize(m->stage_ev);
+  hipEventDestroy(m->stage_ev);
+  hipHostFree(m->h_stage);
+  for (hipEvent_t e : m->ev) hipEventDestroy(e);
+  delete m;
+  return TTE_OK;
+}
+
+tte_status tte_op_layernorm(const float* d_x, const float* d_gamma, int32_t rows, int32_t width, float eps,
+                            int32_t out_kind, void* d_out, float* d_scale, void* stream) {
+  if (rows < 0) return fail(TTE_E_INVALID, "rows must be >= 0");
+  if (!row_width_supported(width)) return fail(TTE_E_UNSUPPORTED, "unsupported row width");
+  if (out_kind < TTE_OUT_F32 || out_kind > TTE_OUT_I8) return fail(TTE_E_INVALID, "bad out_kind");
+  if (rows == 0) return TTE_OK;
+  if (!d_x || !d_out || (out_kind == TTE_OUT_I8 && !d_scale)) return fail(TTE_E_INVALID, "NULL buffer");
+  if (d_gamma && !(eps > 0.f)) return fail(TTE_E_INVALID, "eps must be > 0");
+  (void)hipGetLastError();
+  launch_ln(d_x, d_gamma, rows, width, eps, out_kind, d_out, d_scale, reinterpret_cast<hipStream_t>(stream));
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+tte_status tte_op_quant7(const float* d_x, int32_t rows, int32_t width, int8_t* d_q, float* d_scale, void* stream) {
+  if (rows < 0) return fail(TTE_E_INVALID, "rows must be >= 0");
+  if (!row_width_supported(width)) return fail(TTE_E_UNSUPPORTED, "unsupported row width");
+  if (rows == 0) return TTE_OK;
+  if (!d_x || !d_q || !d_scale) return fail(TTE_E_INVALID, "NULL buffer");
+  (void)hipGetLastError();
+  launch_quant7(d_x, rows, width, d_q, d_scale, reinterpret_cast<hipStream_t>(stream));
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, const float* d_a_scale, const void* d_w,
+                       const float* d_w_scale, int32_t M, int32_t N, int32_t K, void* d_c, int32_t out_kind,
+                       void* stream) {
+  if (precision < TTE_FP32 || precision > TTE_INT8) return fail(TTE_E_INVALID, "bad precision");
+  if (epilogue < TTE_EPI_STORE || epilogue > TTE_EPI_GEGLU) return fail(TTE_E_INVALID, "bad epilogue");
+  if (M < 0 || N <= 0 || K <= 0) return fail(TTE_E_INVALID, "M must be >= 0, N and K > 0");
+  if (K % 128 != 0) return fail(TTE_E_UNSUPPORTED, "K must be a multiple of 128");
+  if (epilogue == TTE_EPI_GEGLU ? (N % 64 != 0) : (N % 128 != 0))
+    return fail(TTE_E_UNSUPPORTED, "N must be a multiple of 128 (64 for GEGLU)");
+  if (out_kind != TTE_OUT_F32 && out_kind != TTE_OUT_BF16) return fail(TTE_E_INVALID, "out_kind must be F32 or BF16");
+  if (epilogue == TTE_EPI_RESIDUAL && out_kind != TTE_OUT_F32) return fail(TTE_E_INVALID, "RESIDUAL needs fp32 C");
+  if (M == 0) return TTE_OK;
+  if (!d_a || !d_w || !d_c) return fail(TTE_E_INVALID, "NULL buffer");
+  if (precision == TTE_INT8 && (!d_a_scale || !d_w_scale)) return fail(TTE_E_INVALID, "int8 needs both scales");
+  (void)hipGetLastError();
+  launch_gemm(precision, epilogue, d_a, d_a_scale, d_w, d_w_scale, M, N, K, d_c, out_kind,
+              reinterpret_cast<hipStream_t>(stream));
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+tte_status tte_op_attention(tte_model* m, int32_t layer, const void* d_qkv, int32_t n_tokens, const int32_t* h_offsets,
+                            int32_t n_texts, void* d_o, void* stream) {
+  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+  if (layer < 0 || layer >= m->cfg.n_layers) return fail(TTE_E_INVALID, "layer out of range");
+  tte_status st = check_pack(m->cfg, n_tokens, h_offsets, n_texts);
+  if (st != TTE_OK) return st;
+  if (n_texts == 0) return TTE_OK;
+  if (!d_qkv || !d_o) return fail(TTE_E_INVALID, "NULL buffer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  int n_units = 0;
+  st = upload_pack(m, h_offsets, n_texts, &n_units, s);
+  if (st != TTE_OK) return st;
+  k_seg<<<(n_tokens + 255) / 256, 256, 0, s>>>(m->d_off, n_texts, n_tokens, m->seg);
+  const int glob = (layer % m->cfg.global_every) == 0;
+  launch_attention(m->cfg.precision == TTE_BF16 ? P_BF16 : P_F32, d_qkv, d_o, m->seg, glob ? m->cosg : m->cosl,
+                   glob ? m->sing : m->sinl, n_tokens, m->cfg.n_heads, glob, m->cfg.window, s);
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+tte_status tte_op_pool(tte_model* m, const float* d_x, int32_t n_tokens, const int32_t* h_offsets, int32_t n_texts,
+                       float* d_out, void* stream) {
+  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+  tte_status st = check_pack(m->cfg, n_tokens, h_offsets, n_texts);
+  if (st != TTE_OK) return st;
+  if (n_texts == 0) return TTE_OK;
+  if (!d_x || !d_out) return fail(TTE_E_INVALID, "NULL buffer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  int n_units = 0;
+  st = upload_pack(m, h_offsets, n_texts, &n_units, s);
+  if (st != TTE_OK) return st;
+  launch_pool(d_x, m->w.final_norm, m->cfg.ln_eps, m->cfg.hidden, m->d_off, m->d_unit, n_texts, n_units, m->partial,
+              d_out, s);
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+tte_status tte_profile_start(tte_model* m, uint32_t class_mask, int32_t max_launches) {
+  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+  if (max_launches <= 0) return fail(TTE_E_INVALID, "max_launches must be positive");
+  for (hipEvent_t e : m->ev) hipEventDestroy(e);
+  m->ev.assign(2 * (size_t)max_launches, nullptr);
+  m->ev_cls.assign((size_t)max_launches, 0);
+  for (auto& e : m->ev) {
+    tte_status st = hip_check(hipEventCreate(&e), "hipEventCreate");
+    if (st != TTE_OK) return st;
+  }
+  m->ev_used = 0;
+  m->ev_overflow = false;
+  m->prof_mask = class_mask;
+  m->prof_on = true;
+  return TTE_OK;
+}
+
+tte_status tte_profile_stop(tte_model* m, double* ms_per_class, int64_t* launches_per_class) {
+  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+  if (!ms_per_class || !launches_per_class) return fail(TTE_E_INVALID, "NULL output");
+  m->prof_on = false;
+  for (int k = 0; k < TTE_K_COUNT; ++k) {
+    ms_per_class[k] = 0.0;
+    launches_per_class[k] = 0;
+  }
+  for (int i = 0; i < m->ev_used; ++i) {
+    tte_status st = hip_check(hipEventSynchronize(m->ev[2 * i + 1]), "hipEventSynchronize");
+    if (st != TTE_OK) return st;
+    float ms = 0.f;
+    st = hip_check(hipEventElapsedTime(&ms, m->ev[2 * i], m->ev[2 * i + 1]), "hipEventElapsedTime");
+    if (st != TTE_OK) return st;
+    ms_per_class[m->ev_cls[i]] += ms;
+    launches_per_class[m->ev_cls[i]] += 1;
+  }
+  for (hipEvent_t e : m->ev) hipEventDestroy(e);
+  m->ev.clear();
+  m->ev_used = 0;
+  if (m->ev_overflow) return fail(TTE_E_NOMEM, "more launches than max_launches: later ones were not timed");
+  return TTE_OK;
+}
+
+}  // extern "C"

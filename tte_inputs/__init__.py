@@ -261,8 +261,11 @@ class Pack:
 
 
 def text_ids(rng: np.random.Generator, n: int, vocab: int) -> np.ndarray:
-    """One text of n tokens: BOS, n-2 ids uniform in [4, vocab), EOS."""
-    assert n >= 2
+    """One text of n tokens: BOS, n-2 ids uniform in [4, vocab), EOS
+    (a 1-token text is BOS alone)."""
+    assert n >= 1
+    if n == 1:
+        return np.array([BOS], np.int32)
     mid = rng.integers(FIRST_ORDINARY_ID, vocab, size=n - 2)
     return np.concatenate([[BOS], mid, [EOS]]).astype(np.int32)
 
