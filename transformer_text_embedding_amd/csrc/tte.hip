@@ -133,10 +133,12 @@ struct tte_model {
   int* d_unit;
   float* partial;
   const float *cosg, *sing, *cosl, *sinl;
-  // pinned staging for the per-call offsets upload
+  // pinned staging for the per-call offsets upload: a ring of slots, each
+  // reused only after the copy that read it has completed
   int* h_stage;
-  hipEvent_t stage_ev;
-  bool stage_pending;
+  hipEvent_t stage_ev[8];
+  bool stage_pending[8];
+  int stage_next;
   // profiling
   bool prof_on;
   uint32_t prof_mask;
@@ -160,10 +162,10 @@ struct ProfScope {
     }
     idx = m->ev_used++;
     m->ev_cls[idx] = cls;
-    hipEventRecord(m->ev[2 * idx], s);
+    (void)hipEventRecord(m->ev[2 * idx], s);
   }
   ~ProfScope() {
-    if (idx >= 0) hipEventRecord(m->ev[2 * idx + 1], s);
+    if (idx >= 0) (void)hipEventRecord(m->ev[2 * idx + 1], s);
   }
 };
 
@@ -174,14 +176,18 @@ tte_status hip_check(hipError_t e, const char* what) {
 
 // Copies offsets and pool-unit starts into the workspace (stream-ordered,
 // from pinned staging that is reused only once the previous copy is done).
+constexpr int STAGE_SLOTS = 8;
+
 tte_status upload_pack(tte_model* m, const int32_t* h_off, int n_texts, int* n_units, hipStream_t s) {
-  if (m->stage_pending) {
-    tte_status st = hip_check(hipEventSynchronize(m->stage_ev), "hipEventSynchronize");
+  const int slot = m->stage_next;
+  m->stage_next = (slot + 1) % STAGE_SLOTS;
+  if (m->stage_pending[slot]) {
+    tte_status st = hip_check(hipEventSynchronize(m->stage_ev[slot]), "hipEventSynchronize");
     if (st != TTE_OK) return st;
-    m->stage_pending = false;
+    m->stage_pending[slot] = false;
   }
-  int* so = m->h_stage;
-  int* su = m->h_stage + (m->cfg.max_texts + 1);
+  int* so = m->h_stage + (size_t)slot * 2 * (m->cfg.max_texts + 1);
+  int* su = so + (m->cfg.max_texts + 1);
   std::memcpy(so, h_off, sizeof(int) * (size_t)(n_texts + 1));
   su[0] = 0;
   for (int b = 0; b < n_texts; ++b) su[b + 1] = su[b] + (h_off[b + 1] - h_off[b] + POOL_ROWS - 1) / POOL_ROWS;
@@ -192,9 +198,9 @@ tte_status upload_pack(tte_model* m, const int32_t* h_off, int n_texts, int* n_u
   st = hip_check(hipMemcpyAsync(m->d_unit, su, sizeof(int) * (n_texts + 1), hipMemcpyHostToDevice, s),
                  "hipMemcpyAsync(units)");
   if (st != TTE_OK) return st;
-  st = hip_check(hipEventRecord(m->stage_ev, s), "hipEventRecord");
+  st = hip_check(hipEventRecord(m->stage_ev[slot], s), "hipEventRecord");
   if (st != TTE_OK) return st;
-  m->stage_pending = true;
+  m->stage_pending[slot] = true;
   return TTE_OK;
 }
 
@@ -242,7 +248,7 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
     launch_embed_ln(P, d_ids, T, m->w.tok_emb, m->w.tok_emb_scale, c.vocab, m->w.emb_norm, c.ln_eps, H, m->d_off, B,
                     m->x, m->seg, s);
   }
-  if (d_states) hipMemcpyAsync(d_states, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
+  if (d_states) (void)hipMemcpyAsync(d_states, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
 
   for (int l = 0; l < n_run; ++l) {
     const tte_layer_weights& LW = m->layers[l];
@@ -292,7 +298,7 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
       ProfScope ps(m, TTE_K_GEMM_O2, s);
       launch_gemm(P, E_RESID, y_in, m->ascale, LW.wo2, LW.wo2_scale, T, H, I, m->x, O_F32, s);
     }
-    if (d_states) hipMemcpyAsync(d_states + (size_t)(l + 1) * T * H, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
+    if (d_states) (void)hipMemcpyAsync(d_states + (size_t)(l + 1) * T * H, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
   }
   if (n_run == c.n_layers) {
     ProfScope ps(m, TTE_K_POOL, s);
@@ -356,7 +362,7 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   m->w.layers = m->layers.data();
   m->L = L;
   m->ws = reinterpret_cast<uint8_t*>(d_workspace);
-  hipGetDevice(&m->device);
+  (void)hipGetDevice(&m->device);
   uint8_t* b = m->ws;
   m->x = reinterpret_cast<float*>(b + L.x);
   m->xa = b + L.xa;
@@ -390,11 +396,15 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   for (int i = 0; i < 4 && st == TTE_OK; ++i)
     st = hip_check(hipMemcpy(b + dst[i], tab.data() + i * n, n * 4, hipMemcpyHostToDevice), "hipMemcpy(rope)");
   if (st == TTE_OK)
-    st = hip_check(hipHostMalloc((void**)&m->h_stage, sizeof(int) * 2 * ((size_t)c.max_texts + 1), hipHostMallocDefault),
+    st = hip_check(hipHostMalloc((void**)&m->h_stage, sizeof(int) * 2 * ((size_t)c.max_texts + 1) * STAGE_SLOTS,
+                                 hipHostMallocDefault),
                    "hipHostMalloc");
-  if (st == TTE_OK) st = hip_check(hipEventCreateWithFlags(&m->stage_ev, hipEventDisableTiming), "hipEventCreate");
+  int n_ev = 0;
+  for (; st == TTE_OK && n_ev < STAGE_SLOTS; ++n_ev)
+    st = hip_check(hipEventCreateWithFlags(&m->stage_ev[n_ev], hipEventDisableTiming), "hipEventCreate");
   if (st != TTE_OK) {
-    if (m->h_stage) hipHostFree(m->h_stage);
+    for (int i = 0; i + 1 < n_ev; ++i) (void)hipEventDestroy(m->stage_ev[i]);
+    if (m->h_stage) (void)hipHostFree(m->h_stage);
     delete m;
     return st;
   }
@@ -415,10 +425,12 @@ tte_status tte_embed_trace(tte_model* m, const int32_t* d_token_ids, int32_t n_t
 
 tte_status tte_destroy(tte_model* m) {
   if (!m) return fail(TTE_E_INVALID, "model is NULL");
-  if (m->stage_pending) hipEventSynchronize(m->stage_ev);
-  hipEventDestroy(m->stage_ev);
-  hipHostFree(m->h_stage);
-  for (hipEvent_t e : m->ev) hipEventDestroy(e);
+  for (int i = 0; i < STAGE_SLOTS; ++i) {
+    if (m->stage_pending[i]) (void)hipEventSynchronize(m->stage_ev[i]);
+    (void)hipEventDestroy(m->stage_ev[i]);
+  }
+  (void)hipHostFree(m->h_stage);
+  for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
   delete m;
   return TTE_OK;
 }
@@ -506,11 +518,11 @@ tte_status tte_op_pool(tte_model* m, const float* d_x, int32_t n_tokens, const i
 tte_status tte_profile_start(tte_model* m, uint32_t class_mask, int32_t max_launches) {
   if (!m) return fail(TTE_E_INVALID, "model is NULL");
   if (max_launches <= 0) return fail(TTE_E_INVALID, "max_launches must be positive");
-  for (hipEvent_t e : m->ev) hipEventDestroy(e);
+  for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
   m->ev.assign(2 * (size_t)max_launches, nullptr);
   m->ev_cls.assign((size_t)max_launches, 0);
   for (auto& e : m->ev) {
-    tte_status st = hip_check(hipEventCreate(&e), "hipEventCreate");
+    tte_status st = hip_check(hipEventCreateWithFlags(&e, hipEventDisableSystemFence), "hipEventCreate");
     if (st != TTE_OK) return st;
   }
   m->ev_used = 0;
@@ -537,7 +549,7 @@ tte_status tte_profile_stop(tte_model* m, double* ms_per_class, int64_t* launche
     ms_per_class[m->ev_cls[i]] += ms;
     launches_per_class[m->ev_cls[i]] += 1;
   }
-  for (hipEvent_t e : m->ev) hipEventDestroy(e);
+  for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
   m->ev.clear();
   m->ev_used = 0;
   if (m->ev_overflow) return fail(TTE_E_NOMEM, "more launches than max_launches: later ones were not timed");
