@@ -279,3 +279,58 @@ def test_pool(lengths):
     ref = oracle.mean_pool_l2(oracle.layer_norm(x, w["final_norm"], 1e-5), off)
     np.testing.assert_allclose(host(out), ref, atol=2e-6, rtol=0)
     m.close()
+
+
+# --------------------------------------------------------------------------
+# QKV projection with the fused RoPE / transposed-V epilogue
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("precision", ["fp32", "bf16", "int8"])
+@pytest.mark.parametrize("lengths", [[8, 40, 130], [1, 64, 65, 300, 3]])
+@pytest.mark.parametrize("layer", [0, 1])
+def test_qkv_rope_epilogue(precision, lengths, layer):
+    t = torch()
+    heads = 12
+    m = _attn_model(precision, 64 * heads, heads)
+    cfg = m.spec
+    w = ti.storage_weights(ti.EncoderConfig(name="attn", seed=9, **{k: cfg[k] for k in (
+        "vocab", "hidden", "heads", "head_dim", "intermediate", "layers", "precision", "global_every", "window",
+        "rope_base_global", "rope_base_local", "ln_eps")}))
+    L = w["layers"][layer]
+    T, H = sum(lengths), 64 * heads
+    off = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)
+    rng = np.random.default_rng(T + layer)
+    x = rng.normal(size=(T, H)).astype(np.float32)
+    if precision == "int8":
+        qx, sx = oracle.quantize_rows_7bit(x)
+        da, ds = dev(qx), dev(sx)
+        raw = oracle.block_matmul_int8(qx, sx, L["wqkv_q"], L["wqkv_s"])
+    elif precision == "bf16":
+        xb = ti.bf16_bits(x)
+        da, ds = dev(xb), None
+        raw = ti.bf16_to_f32(xb).astype(np.float64) @ oracle.decode_matrix(L, "wqkv", "bf16").T
+    else:
+        da, ds = dev(x), None
+        raw = x.astype(np.float64) @ oracle.decode_matrix(L, "wqkv", "fp32").T
+    is_global = layer % 3 == 0
+    base = 160000.0 if is_global else 10000.0
+    pos = oracle.positions(off)
+    q = oracle.rope(raw[:, :H].reshape(T, heads, 64), pos, base).reshape(T, H)
+    k = oracle.rope(raw[:, H:2 * H].reshape(T, heads, 64), pos, base).reshape(T, H)
+    vT = raw[:, 2 * H:].T
+    dt = t.int16 if precision == "bf16" else t.float32
+    qk = empty((T, 3 * H), dt)
+    vt = empty((H, T), dt)
+    B.tte_op_qkv(m.handle, layer, da.data_ptr(), ds.data_ptr() if ds is not None else 0, T, off, qk.data_ptr(),
+                 vt.data_ptr(), stream())
+    got_qk, got_vt = host(qk), host(vt)
+    if precision == "bf16":
+        got_qk = ti.bf16_to_f32(got_qk.view(np.uint16)).astype(np.float64)
+        got_vt = ti.bf16_to_f32(got_vt.view(np.uint16)).astype(np.float64)
+        tol = dict(rtol=2.0 ** -8, atol=1e-5)
+    else:
+        tol = dict(rtol=1e-5, atol=2e-5 * np.abs(raw).max())
+    np.testing.assert_allclose(got_qk[:, :H], q, **tol)
+    np.testing.assert_allclose(got_qk[:, H:2 * H], k, **tol)
+    np.testing.assert_allclose(got_vt, vT, **tol)
+    m.close()

@@ -58,6 +58,8 @@ _SIGS = {
                               c_void_p, c_int32, c_void_p]),
     "tte_op_attention": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p,
                                    c_void_p]),
+    "tte_op_qkv": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p,
+                             c_void_p, c_void_p]),
     "tte_op_pool": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p, c_void_p]),
     "tte_profile_start": (c_int32, [c_void_p, c_uint32, c_int32]),
     "tte_profile_stop": (c_int32, [c_void_p, POINTER(c_double), POINTER(c_int64)]),
@@ -164,6 +166,13 @@ def tte_op_attention(model: int, layer: int, d_qkv: int, n_tokens: int, offsets,
     arr = int32_array(offsets)
     check(lib().tte_op_attention(c_void_p(model), layer, c_void_p(d_qkv), n_tokens, arr, len(offsets) - 1,
                                  c_void_p(d_o), c_void_p(stream)))
+
+
+def tte_op_qkv(model: int, layer: int, d_a: int, d_a_scale: int, n_tokens: int, offsets, d_qk: int, d_vt: int,
+               stream: int) -> None:
+    arr = int32_array(offsets)
+    check(lib().tte_op_qkv(c_void_p(model), layer, c_void_p(d_a), c_void_p(d_a_scale) if d_a_scale else None,
+                           n_tokens, arr, len(offsets) - 1, c_void_p(d_qk), c_void_p(d_vt), c_void_p(stream)))
 
 
 def tte_op_pool(model: int, d_x: int, n_tokens: int, offsets, d_out: int, stream: int) -> None:

@@ -60,6 +60,11 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stdout}{r.stderr}")
+    try:  # every kernel stub and export must resolve
+        import ctypes
+        ctypes.CDLL(tmp)
+    except OSError as e:
+        raise RuntimeError(f"built library does not load: {e}")
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -10,11 +10,23 @@ namespace tte {
 
 enum Prec { P_F32 = 0, P_BF16 = 1, P_I8 = 2 };
 enum OutKind { O_F32 = 0, O_BF16 = 1, O_I8 = 2 };
-enum Epi { E_STORE = 0, E_RESID = 1, E_GEGLU = 2 };
+enum Epi { E_STORE = 0, E_RESID = 1, E_GEGLU = 2, E_QKV = 3 };
 
 // Per-token text bounds: seg[t] = {offsets[b], offsets[b+1]} of t's text.
 struct Seg {
   int start, end;
+};
+
+// Extra operands of the QKV projection's epilogue: RoPE of the Q and K
+// columns (positions from the per-token text bounds) and V written
+// transposed, vt[h * 64 + d][t] with row stride vt_stride tokens.
+struct QkvOut {
+  const Seg* seg;
+  const float* cos_tab;
+  const float* sin_tab;
+  void* vt;
+  int vt_stride;
+  int hidden;
 };
 
 // Row widths (H or I) the row kernels handle: multiples of 64 with
@@ -41,9 +53,21 @@ void launch_quant7(const float* x, int rows, int width, int8_t* q, float* scale,
 void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const void* W, const float* w_scale,
                  int M, int N, int K, void* C, int out_kind, hipStream_t s);
 
-// Attention over the packed axis; qkv [T, 3H] -> o [T, H] (fp32 or bf16).
-void launch_attention(int prec, const void* qkv, void* o, const Seg* seg, const float* cos_tab,
-                      const float* sin_tab, int T, int n_heads, int is_global, int window, hipStream_t s);
+// QKV projection with the RoPE / transposed-V epilogue: writes rotated Q
+// and K into qkv [M, 3H] (columns 0 .. 2H-1) and V into qo.vt.  Requires
+// the per-token text bounds of the pack in qo.seg.
+void launch_gemm_qkv(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
+                     int K, void* qkv, int out_kind, const QkvOut& qo, hipStream_t s);
+
+// The same RoPE and V transposition from an unrotated qkv [T, 3H] (for the
+// single-kernel attention entry point).
+void launch_qkv_prep(int prec, const void* qkv_in, void* qk_out, const QkvOut& qo, int T, hipStream_t s);
+
+// Attention over the packed axis.  qk: [T, 3H] with rotated Q and K in
+// columns 0 .. 2H-1; vt: V transposed [H][vt_stride]; o: [T, H].  fp32 or
+// bf16 operands.
+void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, void* o, const Seg* seg, int T,
+                      int n_heads, int is_global, int window, hipStream_t s);
 
 // Final LayerNorm + mean per text + L2.  Units of up to POOL_ROWS rows of
 // one text: unit_start[b] .. unit_start[b+1] belong to text b.

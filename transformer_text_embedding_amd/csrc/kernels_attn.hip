@@ -1,5 +1,4 @@
-// Attention over a pack of texts, one head per block column, with RoPE
-// applied to Q and K as they are loaded.
+// Attention over a pack of texts, one head per block column.
 //
 // What it computes (tensai "テキスト埋め込み" page, section 何が動くか):
 // every token attends to the tokens of its own text in both directions; on
@@ -9,22 +8,27 @@
 // (encoder paragraph).  Score = q.k / sqrt(64), softmax over the allowed
 // keys, output = sum of p * v.
 //
+// Inputs come from the QKV projection's epilogue: Q and K already rotated
+// (RoPE applied once per token, in fp32, before rounding), V transposed to
+// vt[h*64 + d][t].  Texts are contiguous token ranges, so "same text" is
+// simply start(q) <= key < end(q); no per-key lookup is needed.
+//
 // How: flash-style streaming over the packed token axis.  A block takes 64
 // consecutive queries (they may span several texts) and walks 64-key tiles
-// over the union of their allowed key ranges only: for a local layer that
-// is at most 64 + 2*window keys, for a global one the texts the queries
-// belong to, so fully masked tiles are never visited; a wave additionally
-// skips the matrix work of tiles outside its own 16 queries' window.  Inside
-// a tile the mask is (same text) and (global or |i - j| <= window), taken per
-// element from the per-token text bounds.
+// over the union of their allowed key ranges only (a local layer needs at
+// most 64 + 2*window keys, a global one the texts of its queries), so fully
+// masked tiles are never loaded; a wave also skips the matrix work of tiles
+// outside its own 16 queries' range.  K rows and V^T rows of a tile stream
+// global -> LDS with direct-to-LDS loads into a double buffer (the next
+// tile loads while the current one is used), rows XOR-swizzled by 16-byte
+// chunk so fragment reads are conflict-free.
 //
 // The products are taken transposed, S^T = K Q^T and O^T = V^T P^T, so that
 // the matrix-core output layout puts one query per lane column: each lane's
-// scores of its query are then directly the B operand of the P*V product,
-// and the running max / sum / rescale of a query live in the lanes that hold
-// it, with two cross-lane steps per reduction.  Softmax uses exp2 with
-// log2(e)/8 folded into one multiply.  fp32 variant: v_mfma_f32_16x16x4_f32;
-// bf16 variant: v_mfma_f32_16x16x32_bf16 with Q, K (after RoPE), V and P
+// scores of its query are directly the B operand of the P*V product, and the
+// running max / sum / rescale of a query stay in the lanes that hold it.
+// Softmax uses exp2 with log2(e)/8 folded into one multiply.  fp32 variant:
+// v_mfma_f32_16x16x4_f32; bf16 variant: v_mfma_f32_16x16x32_bf16 with P
 // rounded to bf16 and all statistics in fp32.
 #include "common.h"
 #include "kernels.h"
@@ -33,38 +37,39 @@ namespace tte {
 
 namespace {
 
-constexpr int AQ = 64;  // queries per block
-constexpr int AKT = 64; // keys per tile
+constexpr int AQ = 64;   // queries per block
+constexpr int AKT = 64;  // keys per tile
 constexpr float NEG_INF = -__builtin_huge_valf();
 
 template <int PREC>
-struct AttnLds;
-
-template <>
-struct AttnLds<P_F32> {
-  float k[AKT][68];   // K tile after RoPE, [key][dim]
-  float vt[64][68];   // V tile transposed, [dim][key]
-  int kseg[AKT];      // text start of each key (-2: outside the range)
+struct AttnCfg {
+  static constexpr int ES = PREC == P_F32 ? 4 : 2;
+  static constexpr int ROWB = 64 * ES;                // bytes of a K row (64 dims) and a V^T row (64 keys)
+  static constexpr int TILE = 2 * 64 * ROWB;          // K tile + V^T tile
+  static constexpr int LDS = 2 * TILE;                // double buffer
+  static constexpr int ROWS_PER_Q = 1024 / ROWB;      // rows per 1 KB load instruction
+  static constexpr int QW = (2 * 64 / ROWS_PER_Q) / 4;  // load instructions per wave per tile
+  static constexpr int ALIGN = 16 / ES;               // key alignment of a V^T row segment
 };
 
-template <>
-struct AttnLds<P_BF16> {
-  uint16_t k[AKT][72];
-  uint16_t vt[64][72];
-  int kseg[AKT];
-};
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
+}
 
 template <int PREC>
-__global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qkv, void* __restrict__ out,
-                                              const Seg* __restrict__ seg, const float* __restrict__ cos_tab,
-                                              const float* __restrict__ sin_tab, int T, int nh, int is_global,
-                                              int window, float scale_log2) {
-  __shared__ AttnLds<PREC> sm;
+__global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const void* __restrict__ vt, int vt_stride,
+                                              void* __restrict__ out, const Seg* __restrict__ seg, int T, int nh,
+                                              int is_global, int window, float scale_log2) {
+  using C = AttnCfg<PREC>;
+  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
   const int H = nh * 64, ld = 3 * H;
   const int h = blockIdx.y;
   const int i0 = blockIdx.x * AQ;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
 
+  // key range of the block (union over its queries) and of this wave
   const int ilast = min(i0 + AQ - 1, T - 1);
   const Seg sa = seg[i0], sb = seg[ilast];
   int kstart = sa.start, kend = sb.end;
@@ -72,146 +77,106 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qkv, void
     kstart = max(kstart, i0 - window);
     kend = min(kend, ilast + window + 1);
   }
-  const int wq_lo = i0 + 16 * w, wq_hi = min(i0 + 16 * w + 15, T - 1);
+  const int wq_lo = min(i0 + 16 * w, T - 1), wq_hi = min(i0 + 16 * w + 15, T - 1);
+  const Seg swl = seg[wq_lo], swh = seg[wq_hi];
+  int wk_lo = swl.start, wk_hi = swh.end;
+  if (!is_global) {
+    wk_lo = max(wk_lo, wq_lo - window);
+    wk_hi = min(wk_hi, wq_hi + window + 1);
+  }
+  const bool wave_any = i0 + 16 * w < T;
 
   const int qi = i0 + 16 * w + li;
   const bool qvalid = qi < T;
   const int qrow = qvalid ? qi : T - 1;
   const Seg qs = seg[qrow];
-  const int qseg = qvalid ? qs.start : -1;
-  const int qpos = qrow - qs.start;
+  const int q_start = qvalid ? qs.start : 0, q_end = qvalid ? qs.end : 0;
 
-  // ---- Q fragment with RoPE (pairs (d, d+32)) ----
-  f32x4 qf[4];      // fp32: dims 16 kc + 4 g + e
-  bf16x8 qb[2];     // bf16: dims 32 kc + 8 g + e
+  // ---- Q fragment (already rotated) ----
+  f32x4 qf[4];   // fp32: dims 16 kc + 4 g + e
+  bf16x8 qb[2];  // bf16: dims 32 kc + 8 g + e
   if constexpr (PREC == P_F32) {
-    const float* qp = reinterpret_cast<const float*>(qkv) + (size_t)qrow * ld + h * 64;
+    const float* qp = reinterpret_cast<const float*>(qk) + (size_t)qrow * ld + h * 64;
 #pragma unroll
     for (int kc = 0; kc < 4; ++kc) qf[kc] = *reinterpret_cast<const f32x4*>(qp + 16 * kc + 4 * g);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc) {
-      const f32x4 c = *reinterpret_cast<const f32x4*>(cos_tab + qpos * 32 + 16 * kc + 4 * g);
-      const f32x4 s = *reinterpret_cast<const f32x4*>(sin_tab + qpos * 32 + 16 * kc + 4 * g);
-      const f32x4 x = qf[kc], y = qf[kc + 2];
-      qf[kc] = x * c - y * s;
-      qf[kc + 2] = y * c + x * s;
-    }
   } else {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(qkv) + (size_t)qrow * ld + h * 64;
-    const u16x8 r0 = *reinterpret_cast<const u16x8*>(qp + 8 * g);
-    const u16x8 r1 = *reinterpret_cast<const u16x8*>(qp + 32 + 8 * g);
-    u16x8 o0, o1;
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(qk) + (size_t)qrow * ld + h * 64;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float c = cos_tab[qpos * 32 + 8 * g + e], s = sin_tab[qpos * 32 + 8 * g + e];
-      const float x = bf16_to_f32(r0[e]), y = bf16_to_f32(r1[e]);
-      o0[e] = f32_to_bf16(x * c - y * s);
-      o1[e] = f32_to_bf16(y * c + x * s);
-    }
-    qb[0] = __builtin_bit_cast(bf16x8, o0);
-    qb[1] = __builtin_bit_cast(bf16x8, o1);
+    for (int kc = 0; kc < 2; ++kc) qb[kc] = *reinterpret_cast<const bf16x8*>(qp + 32 * kc + 8 * g);
   }
+
+  // ---- load plan: instruction j of wave w covers tile rows
+  // ROWS_PER_Q * (w * QW + j) + lane / (ROWB / 16); rows 0..63 are K rows,
+  // rows 64..127 are V^T rows (dims) ----
+  constexpr int CPR = C::ROWB / 16;  // 16-byte chunks per row
+  const int j_first = kstart & ~(C::ALIGN - 1);
+  const int n_tiles = (kend - j_first + AKT - 1) / AKT;
+  auto issue = [&](int t) {
+    uint8_t* stage = smem + (t & 1) * C::TILE;
+    const int j0 = j_first + t * AKT;
+#pragma unroll
+    for (int j = 0; j < C::QW; ++j) {
+      const int q = w * C::QW + j;
+      const int row = C::ROWS_PER_Q * q + lane / CPR;
+      const int chunk = (lane % CPR) ^ (row & 7);
+      const uint8_t* src;
+      if (row < 64) {
+        const int kr = min(j0 + row, T - 1);
+        src = reinterpret_cast<const uint8_t*>(qk) + ((size_t)kr * ld + H + h * 64) * C::ES + chunk * 16;
+      } else {
+        src = reinterpret_cast<const uint8_t*>(vt) + ((size_t)(h * 64 + row - 64) * vt_stride + j0) * C::ES + chunk * 16;
+      }
+      dma16(src, stage + q * 1024);
+    }
+  };
 
   f32x4 oacc[4];
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = NEG_INF, l_run = 0.f;
 
-  for (int j0 = kstart; j0 < kend; j0 += AKT) {
-    __syncthreads();
-    // ---- K tile (RoPE) and transposed V tile into LDS ----
-    if constexpr (PREC == P_F32) {
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int p = tid + 256 * i, key = p >> 3, c = p & 7;
-        const int kj = j0 + key, krow = min(kj, T - 1);
-        const Seg ks = seg[krow];
-        const int kpos = krow - ks.start;
-        const float* kp = reinterpret_cast<const float*>(qkv) + (size_t)krow * ld + H + h * 64;
-        const f32x4 x = *reinterpret_cast<const f32x4*>(kp + 4 * c);
-        const f32x4 y = *reinterpret_cast<const f32x4*>(kp + 32 + 4 * c);
-        const f32x4 cs = *reinterpret_cast<const f32x4*>(cos_tab + kpos * 32 + 4 * c);
-        const f32x4 sn = *reinterpret_cast<const f32x4*>(sin_tab + kpos * 32 + 4 * c);
-        *reinterpret_cast<f32x4*>(&sm.k[key][4 * c]) = x * cs - y * sn;
-        *reinterpret_cast<f32x4*>(&sm.k[key][32 + 4 * c]) = y * cs + x * sn;
-        if (c == 0) sm.kseg[key] = kj < kend ? ks.start : -2;
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int p = tid + 256 * i, key = p >> 4, c4 = p & 15;
-        const int krow = min(j0 + key, T - 1);
-        const f32x4 v =
-            *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(qkv) + (size_t)krow * ld + 2 * H + h * 64 + 4 * c4);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) sm.vt[4 * c4 + e][key] = v[e];
-      }
-    } else {
-      {
-        const int key = tid >> 2, c = tid & 3;
-        const int kj = j0 + key, krow = min(kj, T - 1);
-        const Seg ks = seg[krow];
-        const int kpos = krow - ks.start;
-        const uint16_t* kp = reinterpret_cast<const uint16_t*>(qkv) + (size_t)krow * ld + H + h * 64;
-        const u16x8 x = *reinterpret_cast<const u16x8*>(kp + 8 * c);
-        const u16x8 y = *reinterpret_cast<const u16x8*>(kp + 32 + 8 * c);
-        u16x8 o0, o1;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float cs = cos_tab[kpos * 32 + 8 * c + e], sn = sin_tab[kpos * 32 + 8 * c + e];
-          const float xf = bf16_to_f32(x[e]), yf = bf16_to_f32(y[e]);
-          o0[e] = f32_to_bf16(xf * cs - yf * sn);
-          o1[e] = f32_to_bf16(yf * cs + xf * sn);
-        }
-        *reinterpret_cast<u16x8*>(&sm.k[key][8 * c]) = o0;
-        *reinterpret_cast<u16x8*>(&sm.k[key][32 + 8 * c]) = o1;
-        if (c == 0) sm.kseg[key] = kj < kend ? ks.start : -2;
-      }
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int p = tid + 256 * i, key = p >> 3, c8 = p & 7;
-        const int krow = min(j0 + key, T - 1);
-        const u16x8 v = *reinterpret_cast<const u16x8*>(reinterpret_cast<const uint16_t*>(qkv) + (size_t)krow * ld +
-                                                        2 * H + h * 64 + 8 * c8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sm.vt[8 * c8 + e][key] = v[e];
-      }
-    }
-    __syncthreads();
-
-    if (!is_global && (j0 > wq_hi + window || j0 + AKT - 1 < wq_lo - window)) continue;
+  if (n_tiles > 0) issue(0);
+  for (int t = 0; t < n_tiles; ++t) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile t (and Q) are done
+    __builtin_amdgcn_s_barrier();        // every wave's are; tile t - 1's buffer is free
+    if (t + 1 < n_tiles) issue(t + 1);
+    const int j0 = j_first + t * AKT;
+    if (!wave_any || j0 >= wk_hi || j0 + AKT <= wk_lo) continue;
+    const uint8_t* Ks = smem + (t & 1) * C::TILE;
+    const uint8_t* Vs = Ks + 64 * C::ROWB;
 
     // ---- S^T = K Q^T: lane holds keys 16 mt + 4 g + r of query li ----
     f32x4 sacc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
       sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const uint8_t* kr = Ks + (16 * mt + li) * C::ROWB;
       if constexpr (PREC == P_F32) {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.k[16 * mt + li][16 * kc + 4 * g]);
+          const f32x4 a = *reinterpret_cast<const f32x4*>(kr + (((4 * kc + g) ^ (li & 7)) << 4));
 #pragma unroll
           for (int s = 0; s < 4; ++s) sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], qf[kc][s], sacc[mt], 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sm.k[16 * mt + li][32 * kc + 8 * g]);
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((4 * kc + g) ^ (li & 7)) << 4));
           sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[kc], sacc[mt], 0, 0, 0);
         }
       }
     }
 
-    // ---- mask, online softmax ----
+    // ---- mask (same text: q_start <= key < q_end; window), online softmax ----
     float sv[16];
     float mloc = NEG_INF;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int kk = 16 * mt + 4 * g + r;
-        const int kj = j0 + kk;
+        const int kj = j0 + 16 * mt + 4 * g + r;
         const int d = qi - kj;
-        const bool ok = (sm.kseg[kk] == qseg) && (is_global || (d <= window && -d <= window));
+        const bool ok = kj >= q_start && kj < q_end && (is_global || (d <= window && -d <= window));
         sv[mt * 4 + r] = ok ? sacc[mt][r] : NEG_INF;
         mloc = fmaxf(mloc, sv[mt * 4 + r]);
       }
@@ -237,35 +202,41 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qkv, void
     // ---- O^T += V^T P^T ----
     if constexpr (PREC == P_F32) {
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint8_t* vr = Vs + (16 * dt + li) * C::ROWB;
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt) {
-          const f32x4 a = *reinterpret_cast<const f32x4*>(&sm.vt[16 * dt + li][16 * mt + 4 * g]);
+          const f32x4 a = *reinterpret_cast<const f32x4*>(vr + (((4 * mt + g) ^ (li & 7)) << 4));
 #pragma unroll
           for (int r = 0; r < 4; ++r)
             oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], sv[mt * 4 + r], oacc[dt], 0, 0, 0);
         }
+      }
     } else {
       bf16x8 pb[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        u16x8 t;
+        u16x8 tt;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          t[e] = f32_to_bf16(sv[(2 * u) * 4 + e]);
-          t[4 + e] = f32_to_bf16(sv[(2 * u + 1) * 4 + e]);
+          tt[e] = f32_to_bf16(sv[(2 * u) * 4 + e]);
+          tt[4 + e] = f32_to_bf16(sv[(2 * u + 1) * 4 + e]);
         }
-        pb[u] = __builtin_bit_cast(bf16x8, t);
+        pb[u] = __builtin_bit_cast(bf16x8, tt);
       }
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint8_t* vr = Vs + (16 * dt + li) * C::ROWB;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          const u16x4 lo = *reinterpret_cast<const u16x4*>(&sm.vt[16 * dt + li][32 * u + 4 * g]);
-          const u16x4 hi = *reinterpret_cast<const u16x4*>(&sm.vt[16 * dt + li][32 * u + 16 + 4 * g]);
-          const u16x8 t = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, t), pb[u], oacc[dt], 0, 0, 0);
+          // keys 32u + 4g .. +3 and 32u + 16 + 4g .. +3 (the key order of pb)
+          const u16x4 lo = *reinterpret_cast<const u16x4*>(vr + (((4 * u + (g >> 1)) ^ (li & 7)) << 4) + ((g & 1) << 3));
+          const u16x4 hi =
+              *reinterpret_cast<const u16x4*>(vr + (((4 * u + 2 + (g >> 1)) ^ (li & 7)) << 4) + ((g & 1) << 3));
+          const u16x8 tt = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tt), pb[u], oacc[dt], 0, 0, 0);
         }
+      }
     }
   }
 
@@ -280,24 +251,66 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qkv, void
     uint16_t* op = reinterpret_cast<uint16_t*>(out) + (size_t)qi * H + h * 64;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const u16x4 t = {f32_to_bf16(oacc[dt][0] * inv_l), f32_to_bf16(oacc[dt][1] * inv_l),
-                       f32_to_bf16(oacc[dt][2] * inv_l), f32_to_bf16(oacc[dt][3] * inv_l)};
-      *reinterpret_cast<u16x4*>(op + 16 * dt + 4 * g) = t;
+      const u16x4 tt = {f32_to_bf16(oacc[dt][0] * inv_l), f32_to_bf16(oacc[dt][1] * inv_l),
+                        f32_to_bf16(oacc[dt][2] * inv_l), f32_to_bf16(oacc[dt][3] * inv_l)};
+      *reinterpret_cast<u16x4*>(op + 16 * dt + 4 * g) = tt;
     }
   }
 }
 
+// RoPE of Q and K and transposition of V from an unrotated qkv (the same
+// arithmetic as the QKV projection's epilogue): one thread per token and
+// (head, pair) index c < H/2.
+template <int PREC>
+__global__ __launch_bounds__(256) void k_qkv_prep(const void* __restrict__ in, void* __restrict__ qk_out, QkvOut qo,
+                                                  int T) {
+  const int H = qo.hidden, half = H / 2;
+  const long idx = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (long)T * half) return;
+  const int t = (int)(idx / half), c = (int)(idx % half);
+  const int h = c / 32, d = c % 32;
+  const int pos = t - qo.seg[t].start;
+  const float cs = qo.cos_tab[pos * 32 + d], sn = qo.sin_tab[pos * 32 + d];
+  const size_t row = (size_t)t * 3 * H;
+  auto ld = [&](size_t i) -> float {
+    if constexpr (PREC == P_F32) return reinterpret_cast<const float*>(in)[i];
+    else return bf16_to_f32(reinterpret_cast<const uint16_t*>(in)[i]);
+  };
+  auto st = [&](void* base, size_t i, float v) {
+    if constexpr (PREC == P_F32) reinterpret_cast<float*>(base)[i] = v;
+    else reinterpret_cast<uint16_t*>(base)[i] = f32_to_bf16(v);
+  };
+#pragma unroll
+  for (int part = 0; part < 2; ++part) {  // Q, then K
+    const size_t a = row + part * H + h * 64 + d;
+    const float x = ld(a), y = ld(a + 32);
+    st(qk_out, a, x * cs - y * sn);
+    st(qk_out, a + 32, y * cs + x * sn);
+  }
+  const size_t v = row + 2 * H + h * 64 + d;
+  st(qo.vt, (size_t)(h * 64 + d) * qo.vt_stride + t, ld(v));
+  st(qo.vt, (size_t)(h * 64 + d + 32) * qo.vt_stride + t, ld(v + 32));
+}
+
 }  // namespace
 
-void launch_attention(int prec, const void* qkv, void* o, const Seg* seg, const float* cos_tab, const float* sin_tab,
-                      int T, int n_heads, int is_global, int window, hipStream_t s) {
+void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, void* o, const Seg* seg, int T,
+                      int n_heads, int is_global, int window, hipStream_t s) {
   if (T <= 0) return;
   const dim3 grid((T + AQ - 1) / AQ, n_heads);
   const float scale_log2 = 0.125f * 1.4426950408889634f;
   if (prec == P_BF16)
-    k_attn<P_BF16><<<grid, 256, 0, s>>>(qkv, o, seg, cos_tab, sin_tab, T, n_heads, is_global, window, scale_log2);
+    k_attn<P_BF16><<<grid, 256, 0, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global, window, scale_log2);
   else
-    k_attn<P_F32><<<grid, 256, 0, s>>>(qkv, o, seg, cos_tab, sin_tab, T, n_heads, is_global, window, scale_log2);
+    k_attn<P_F32><<<grid, 256, 0, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global, window, scale_log2);
+}
+
+void launch_qkv_prep(int prec, const void* qkv_in, void* qk_out, const QkvOut& qo, int T, hipStream_t s) {
+  if (T <= 0) return;
+  const long n = (long)T * (qo.hidden / 2);
+  const int blocks = (int)((n + 255) / 256);
+  if (prec == P_BF16) k_qkv_prep<P_BF16><<<blocks, 256, 0, s>>>(qkv_in, qk_out, qo, T);
+  else k_qkv_prep<P_F32><<<blocks, 256, 0, s>>>(qkv_in, qk_out, qo, T);
 }
 
 }  // namespace tte

@@ -4,26 +4,40 @@
 // "テキスト埋め込み" page, section 何が動くか (encoder paragraph); the int8
 // form is the integer matmul of its section 精度と量子化.
 //
-// One kernel template serves three operand formats.  Every K tile is 128
-// bytes per row whatever the format (32 fp32, 64 bf16 or 128 int8), so the
-// global->LDS traffic is identical: a 128 x 128 output tile, 256 threads
-// (4 waves in a 2 x 2 grid, each owning 64 x 64 = 4 x 4 MFMA 16x16 tiles),
-// A and W tiles of 128 rows x 128 bytes double-buffered in LDS with rows
-// padded to 144 bytes (16-lane fragment reads land in distinct banks), the
-// next K tile prefetched into registers while the current one is consumed.
+// One kernel template serves three operand formats.  A K tile is 128 bytes
+// of every row whatever the format (32 fp32, 64 bf16 or 128 int8), so the
+// data movement is identical:
+//
+//  * 256 threads, 4 waves in a 2 x 2 grid; a wave owns WM x WN MFMA 16x16
+//    output tiles (block tile BM = 32 WM rows by BN = 32 WN columns).
+//  * K tiles stream global -> LDS with the gfx950 direct-to-LDS load
+//    (global_load_lds_dwordx4: each lane's 16 bytes land in LDS without
+//    passing through registers) into a ring of STAGES buffers (STAGES - 1
+//    tiles in flight while one is consumed).  Each wave waits for its own
+//    oldest loads with s_waitcnt vmcnt(n) and a raw s_barrier publishes
+//    them; no fence drains the other tiles in flight.  Small LDS stages
+//    leave room for several blocks per CU, which overlap one another's
+//    pipeline fill and epilogue.
+//  * LDS rows are 128 bytes, unpadded, with the eight 16-byte chunks of row
+//    r stored at slot chunk ^ (r & 7): the 8 lanes of a fragment read (rows
+//    r..r+7, one chunk) then hit 8 distinct bank groups.
+//  * Blocks are ordered so that the blocks one XCD runs (block id mod 8)
+//    form a contiguous run of the n-major tile order: they share W columns,
+//    which then stay in that XCD's L2.
 //
 //   fp32: v_mfma_f32_16x16x4_f32, 4 per 16-k chunk (each lane reads a float4
 //         and feeds one element per MFMA; A and W use the same k order).
 //   bf16: v_mfma_f32_16x16x32_bf16, one per 32-k chunk, fp32 accumulate.
 //   int8: v_mfma_i32_16x16x32_i8, one per 32-k block (exact int32 sum of the
-//         block), then acc += float(sum) * w_scale[n, block] in fp32; the row
-//         scale a_scale[m] multiplies once in the epilogue.
+//         block), then acc += float(sum) * w_scale[n, block] in fp32; the
+//         block scales of the W tile ride the same LDS ring; the row scale
+//         a_scale[m] multiplies once in the epilogue.
 //
 // Epilogues: STORE (fp32 or bf16), RESID (fp32 C += result), GEGLU.  For
-// GEGLU the W tile rows are chosen so that every wave's first 32 columns
-// are up-projection rows n (the GELU half) and its last 32 are rows I + n
-// (the gate half): the two halves of one output land in the same lane and
-// combine in registers, and the [M, 2I] intermediate is never stored.
+// GEGLU the W tile rows are chosen so that the first half of every wave's
+// columns are up-projection rows n (the GELU half) and the second half rows
+// I + n (the gate half): the two halves of one output land in the same lane
+// and combine in registers, and the [M, 2I] intermediate is never stored.
 #include "common.h"
 #include "kernels.h"
 
@@ -31,11 +45,9 @@ namespace tte {
 
 namespace {
 
-constexpr int BM = 128;
-constexpr int BN = 128;
-constexpr int KT_BYTES = 128;  // bytes of K per tile row
-constexpr int LDS_ROW = 144;   // padded LDS row (bytes)
-constexpr int STAGE = (BM + BN) * LDS_ROW;
+constexpr int KT_BYTES = 128;      // bytes of K per tile row
+constexpr int ROW = 128;           // LDS row (bytes)
+constexpr int SCALE_BYTES = 2048;  // int8: fp32 scales of 4 blocks x 128 W rows
 
 template <int PREC>
 struct Fmt {
@@ -43,179 +55,286 @@ struct Fmt {
   static constexpr int BK = KT_BYTES / ES;
 };
 
-// Row of W that tile row r (0..127) of n-block nb reads.
-template <int EPI>
+template <int WM, int WN, int PREC, int STAGES_ = 4>
+struct Cfg {
+  static constexpr int BM = 32 * WM;
+  static constexpr int BN = 32 * WN;
+  static constexpr int ROWS = BM + BN;
+  static constexpr int TILE = ROWS * ROW + (PREC == P_I8 ? SCALE_BYTES : 0);
+  static constexpr int STAGES = STAGES_;
+  static constexpr int LDS = STAGES * TILE;
+  static constexpr int Q = ROWS / 8;  // 1 KB load instructions per K tile
+  static constexpr int QW = Q / 4;    // per wave
+  static constexpr int PER_TILE = QW + (PREC == P_I8 ? 1 : 0);  // vector-memory ops per wave per tile
+  static_assert(Q % 4 == 0, "tile rows must split evenly over 4 waves");
+  static_assert(PREC != P_I8 || BN == 128, "int8 scale staging assumes 128 W rows");
+  static_assert(LDS <= 160 * 1024, "LDS budget");
+};
+
+// Row of W that tile row r of n-block nb reads.  GEGLU: in each wave's half
+// of the tile (BN/2 rows), the first BN/4 rows are GELU-half rows n and the
+// last BN/4 the matching gate rows N + n.
+template <int EPI, int BN>
 __device__ __forceinline__ int w_row(int r, int nb, int N) {
   if constexpr (EPI == E_GEGLU) {
-    const int half_wave = r >> 6, within = r & 63;
-    const int base = nb * 64 + half_wave * 32;
-    return within < 32 ? base + within : N + base + (within - 32);
+    constexpr int HW = BN / 2, QW_ = BN / 4;
+    const int half_wave = r / HW, within = r % HW;
+    const int base = nb * (BN / 2) + half_wave * QW_;
+    return within < QW_ ? base + within : N + base + (within - QW_);
   } else {
     return nb * BN + r;
   }
 }
 
-// Global -> registers: one 16-byte chunk of 4 A rows and 4 W rows (and, for
-// int8, the lane's 4 weight-scale vectors) of K tile kt.
-template <int PREC>
-__device__ __forceinline__ void fetch_tile(u32x4 (&ra)[4], u32x4 (&rw)[4], f32x4 (&sw)[4], const uint8_t* a_src0,
-                                           const uint8_t* w_src0, const size_t (&a_off)[4], const size_t (&w_off)[4],
-                                           const float* w_scale, const size_t (&s_off)[4], int kt) {
-  const size_t k_off = (size_t)kt * KT_BYTES;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    ra[i] = *reinterpret_cast<const u32x4*>(a_src0 + a_off[i] + k_off);
-    rw[i] = *reinterpret_cast<const u32x4*>(w_src0 + w_off[i] + k_off);
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maxima (gfx9
+// encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define TTE_W(k) \
+  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | ((k) & 15) | ((((k) >> 4) & 3) << 14)); break;
+    TTE_W(0) TTE_W(1) TTE_W(2) TTE_W(3) TTE_W(4) TTE_W(5) TTE_W(6) TTE_W(7) TTE_W(8) TTE_W(9) TTE_W(10)
+    TTE_W(11) TTE_W(12) TTE_W(13) TTE_W(14) TTE_W(15) TTE_W(16) TTE_W(17) TTE_W(18) TTE_W(19) TTE_W(20)
+#undef TTE_W
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
   }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// One direct-to-LDS load: each lane's 16 bytes at g go to LDS l + 16 * lane
+// (l must be the same for the whole wave).  Kept a plain (non-template)
+// function: the builtin inside templated kernels loses the host-side kernel
+// stub in this compiler.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
+}
+
+// Issue the direct-to-LDS loads of K tile kt into `stage`: QW 1 KB
+// instructions of A/W rows, and for int8 the 16-byte scale vectors of 32 W
+// rows (lanes 0..31).
+template <int QW, int PREC>
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* const* src, const float* s_src, int kt,
+                                           int wid, int lane, int rows) {
+#pragma unroll
+  for (int j = 0; j < QW; ++j) dma16(src[j] + (size_t)kt * KT_BYTES, stage + (wid * QW + j) * 1024);
   if constexpr (PREC == P_I8) {
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) sw[nt] = *reinterpret_cast<const f32x4*>(w_scale + s_off[nt] + kt * 4);
+    if (lane < 32) dma16(s_src + kt * 4, stage + rows * ROW + wid * 512);
   }
 }
 
-__device__ __forceinline__ void stash_tile(uint8_t* base, const u32x4 (&ra)[4], const u32x4 (&rw)[4], int lrow,
-                                           int lch) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    *reinterpret_cast<u32x4*>(base + (lrow + 32 * i) * LDS_ROW + lch * 16) = ra[i];
-    *reinterpret_cast<u32x4*>(base + (BM + lrow + 32 * i) * LDS_ROW + lch * 16) = rw[i];
-  }
-}
-
-template <int PREC, int EPI, int OUT>
+template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
                                               const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
-                                              void* __restrict__ C, int M, int N, int K) {
+                                              void* __restrict__ C, int M, int N, int K, int n_blocks,
+                                              int m_blocks, QkvOut qo) {
   using F = Fmt<PREC>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * STAGE];
+  using G = Cfg<WM, WN, PREC, STAGES>;
+  constexpr int BM = G::BM, BN = G::BN;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int wm = wid >> 1, wn = wid & 1;
   const int g = lane >> 4, li = lane & 15;
-  const int nb = blockIdx.x, m0 = blockIdx.y * BM;
+
+  // XCD-aware tile order: block b runs on XCD b mod 8; XCD x gets a
+  // contiguous run of the n-major tile order.
+  const int n_tiles = n_blocks * m_blocks;
+  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int per = n_tiles >> 3, extra = n_tiles & 7;
+  const int tile = xcd * per + min(xcd, extra) + local;
+  const int nb = tile / m_blocks, mb = tile % m_blocks;
+  const int m0 = mb * BM;
   const size_t row_bytes = (size_t)K * F::ES;
   const int nk = K / F::BK;
 
-  // global -> register assignment: rows lrow + 32 i, 16-byte chunk lch
-  const int lrow = tid >> 3, lch = tid & 7;
-  const uint8_t* a_src0 = A + lch * 16;
-  const uint8_t* w_src0 = W + lch * 16;
-  size_t a_off[4], w_off[4];
+  // load plan: instruction j of this wave fills LDS rows 8q .. 8q+7 of the
+  // tile (q = wid * QW + j); lane -> row 8q + lane/8, slot lane%8, which
+  // holds chunk slot ^ (row & 7) = (lane & 7) ^ (lane >> 3).
+  const int chunk = (lane & 7) ^ (lane >> 3);
+  const uint8_t* src[G::QW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    a_off[i] = (size_t)min(m0 + lrow + 32 * i, M - 1) * row_bytes;
-    w_off[i] = (size_t)w_row<EPI>(lrow + 32 * i, nb, N) * row_bytes;
+  for (int j = 0; j < G::QW; ++j) {
+    const int r = 8 * (wid * G::QW + j) + (lane >> 3);
+    if (r < BM)
+      src[j] = A + (size_t)min(m0 + r, M - 1) * row_bytes + chunk * 16;
+    else
+      src[j] = W + (size_t)w_row<EPI, BN>(r - BM, nb, N) * row_bytes + chunk * 16;
   }
+  // int8: lanes 0..31 of wave w load the 4 block scales (16 bytes) of W row
+  // 32 w + lane of the tile.
+  const float* s_src = nullptr;
+  if constexpr (PREC == P_I8) s_src = w_scale + (size_t)w_row<EPI, BN>(wid * 32 + (lane & 31), nb, N) * (K / 32);
 
-  // int8: per-lane weight scales of its 4 column groups, 4 blocks per K tile
-  const int kblocks = K / 32;
-  size_t s_off[4] = {0, 0, 0, 0};
-  if constexpr (PREC == P_I8) {
+  f32x4 acc[WM][WN];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt) s_off[nt] = (size_t)w_row<EPI>(wn * 64 + nt * 16 + li, nb, N) * kblocks;
-  }
-
-  u32x4 ra[4], rw[4];
-  f32x4 sw[4], sw_next[4];
-
-  f32x4 acc[4][4];
+  for (int a = 0; a < WM; ++a)
 #pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int b = 0; b < WN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  fetch_tile<PREC>(ra, rw, sw_next, a_src0, w_src0, a_off, w_off, w_scale, s_off, 0);
-  stash_tile(smem, ra, rw, lrow, lch);
-  __syncthreads();
+  for (int p = 0; p < G::STAGES - 1 && p < nk; ++p)
+    issue_tile<G::QW, PREC>(smem + p * G::TILE, src, s_src, p, wid, lane, G::ROWS);
 
+  const int swz = li & 7;
   for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if constexpr (PREC == P_I8) {
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) sw[nt] = sw_next[nt];
-    }
-    if (kt + 1 < nk) fetch_tile<PREC>(ra, rw, sw_next, a_src0, w_src0, a_off, w_off, w_scale, s_off, kt + 1);
-    const uint8_t* As = smem + cur * STAGE + (wm * 64 + li) * LDS_ROW;
-    const uint8_t* Bs = smem + cur * STAGE + (BM + wn * 64 + li) * LDS_ROW;
+    // this wave's loads of tile kt are done once at most `ahead` tiles of
+    // its own loads remain in flight; the barrier publishes every wave's
+    const int ahead = min(nk - 1 - kt, G::STAGES - 2);
+    wait_vm(ahead * G::PER_TILE);
+    __builtin_amdgcn_s_barrier();
+    // the stage of tile kt - 1 is free: every wave finished reading it
+    if (kt + G::STAGES - 1 < nk)
+      issue_tile<G::QW, PREC>(smem + ((kt + G::STAGES - 1) % G::STAGES) * G::TILE, src, s_src, kt + G::STAGES - 1,
+                              wid, lane, G::ROWS);
 
-    if constexpr (PREC == P_F32) {
+    const uint8_t* stage = smem + (kt % G::STAGES) * G::TILE;
+    const uint8_t* As = stage + (wm * 16 * WM + li) * ROW;
+    const uint8_t* Bs = stage + (BM + wn * 16 * WN + li) * ROW;
+
+    if constexpr (PREC == P_F32 || PREC == P_BF16) {
 #pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        f32x4 af[4], bf[4];
+      for (int cc = 0; cc < 2; ++cc) {
+        const int off = ((4 * cc + g) ^ swz) << 4;
+        if constexpr (PREC == P_F32) {
+          f32x4 af[WM], bf[WN];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          af[t] = *reinterpret_cast<const f32x4*>(As + t * 16 * LDS_ROW + c * 64 + g * 16);
-          bf[t] = *reinterpret_cast<const f32x4*>(Bs + t * 16 * LDS_ROW + c * 64 + g * 16);
+          for (int t = 0; t < WM; ++t) af[t] = *reinterpret_cast<const f32x4*>(As + t * 16 * ROW + off);
+#pragma unroll
+          for (int t = 0; t < WN; ++t) bf[t] = *reinterpret_cast<const f32x4*>(Bs + t * 16 * ROW + off);
+#pragma unroll
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+              for (int nt = 0; nt < WN; ++nt)
+                acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mt][s], bf[nt][s], acc[mt][nt], 0, 0, 0);
+        } else {
+          bf16x8 af[WM], bf[WN];
+#pragma unroll
+          for (int t = 0; t < WM; ++t) af[t] = *reinterpret_cast<const bf16x8*>(As + t * 16 * ROW + off);
+#pragma unroll
+          for (int t = 0; t < WN; ++t) bf[t] = *reinterpret_cast<const bf16x8*>(Bs + t * 16 * ROW + off);
+#pragma unroll
+          for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < WN; ++nt)
+              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
         }
-#pragma unroll
-        for (int s = 0; s < 4; ++s)
-#pragma unroll
-          for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-            for (int nt = 0; nt < 4; ++nt)
-              acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32(af[mt][s], bf[nt][s], acc[mt][nt], 0, 0, 0);
-      }
-    } else if constexpr (PREC == P_BF16) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        bf16x8 af[4], bf[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          af[t] = *reinterpret_cast<const bf16x8*>(As + t * 16 * LDS_ROW + c * 64 + g * 16);
-          bf[t] = *reinterpret_cast<const bf16x8*>(Bs + t * 16 * LDS_ROW + c * 64 + g * 16);
-        }
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt)
-            acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
       }
     } else {
+      const float* sc = reinterpret_cast<const float*>(stage + G::ROWS * ROW);
+      f32x4 sw[WN];
+#pragma unroll
+      for (int nt = 0; nt < WN; ++nt) sw[nt] = *reinterpret_cast<const f32x4*>(sc + 4 * (wn * 16 * WN + nt * 16 + li));
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        long af[4], bf[4];
+        const int off = (((2 * c + (g >> 1)) ^ swz) << 4) + ((g & 1) << 3);
+        long af[WM], bf[WN];
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          af[t] = *reinterpret_cast<const long*>(As + t * 16 * LDS_ROW + c * 32 + g * 8);
-          bf[t] = *reinterpret_cast<const long*>(Bs + t * 16 * LDS_ROW + c * 32 + g * 8);
-        }
+        for (int t = 0; t < WM; ++t) af[t] = *reinterpret_cast<const long*>(As + t * 16 * ROW + off);
 #pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
+        for (int t = 0; t < WN; ++t) bf[t] = *reinterpret_cast<const long*>(Bs + t * 16 * ROW + off);
 #pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
+        for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+          for (int nt = 0; nt < WN; ++nt) {
             const i32x4 p = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[mt], bf[nt], i32x4{0, 0, 0, 0}, 0, 0, 0);
-            const float s = sw[nt][c];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[mt][nt][r] = __builtin_fmaf((float)p[r], s, acc[mt][nt][r]);
+            for (int r = 0; r < 4; ++r) acc[mt][nt][r] = __builtin_fmaf((float)p[r], sw[nt][c], acc[mt][nt][r]);
           }
       }
     }
-
-    if (kt + 1 < nk) stash_tile(smem + (cur ^ 1) * STAGE, ra, rw, lrow, lch);
-    __syncthreads();
   }
 
   // epilogue: lane holds rows 4g + r of column li in every 16 x 16 tile
+  if constexpr (EPI == E_QKV) {
+    static_assert(WN == 4, "QKV epilogue: a wave's 64 columns are one head");
+    const int n_base = nb * BN + wn * 64;
+    if (n_base < 2 * qo.hidden) {
+      // Q or K: rotate the pairs (d, d + 32), d = 16 nt + li, nt = 0, 1
 #pragma unroll
-  for (int mt = 0; mt < 4; ++mt) {
+      for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int m = m0 + wm * 16 * WM + mt * 16 + 4 * g + r;
+          if (m >= M) continue;
+          float rs = 1.f;
+          if constexpr (PREC == P_I8) rs = a_scale[m];
+          const int pos = m - qo.seg[m].start;
+#pragma unroll
+          for (int nt = 0; nt < 2; ++nt) {
+            const int d = nt * 16 + li;
+            const float c = qo.cos_tab[pos * 32 + d], sn = qo.sin_tab[pos * 32 + d];
+            const float x = acc[mt][nt][r] * rs, y = acc[mt][nt + 2][r] * rs;
+            const float xr = x * c - y * sn, yr = y * c + x * sn;
+            if constexpr (OUT == O_BF16) {
+              reinterpret_cast<uint16_t*>(C)[(size_t)m * N + n_base + d] = f32_to_bf16(xr);
+              reinterpret_cast<uint16_t*>(C)[(size_t)m * N + n_base + d + 32] = f32_to_bf16(yr);
+            } else {
+              reinterpret_cast<float*>(C)[(size_t)m * N + n_base + d] = xr;
+              reinterpret_cast<float*>(C)[(size_t)m * N + n_base + d + 32] = yr;
+            }
+          }
+        }
+    } else {
+      // V: transposed, the lane's 4 consecutive tokens of one column at once
+#pragma unroll
+      for (int mt = 0; mt < WM; ++mt) {
+        const int mr = m0 + wm * 16 * WM + mt * 16 + 4 * g;
+        float rs[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (PREC == P_I8) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) rs[r] = mr + r < M ? a_scale[mr + r] : 0.f;
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const size_t at = (size_t)(n_base - 2 * qo.hidden + nt * 16 + li) * qo.vt_stride + mr;
+          if constexpr (OUT == O_BF16) {
+            uint16_t* vp = reinterpret_cast<uint16_t*>(qo.vt) + at;
+            if (mr + 3 < M) {
+              const u16x4 t = {f32_to_bf16(acc[mt][nt][0] * rs[0]), f32_to_bf16(acc[mt][nt][1] * rs[1]),
+                               f32_to_bf16(acc[mt][nt][2] * rs[2]), f32_to_bf16(acc[mt][nt][3] * rs[3])};
+              *reinterpret_cast<u16x4*>(vp) = t;
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (mr + r < M) vp[r] = f32_to_bf16(acc[mt][nt][r] * rs[r]);
+            }
+          } else {
+            float* vp = reinterpret_cast<float*>(qo.vt) + at;
+            if (mr + 3 < M) {
+              *reinterpret_cast<f32x4*>(vp) = f32x4{acc[mt][nt][0] * rs[0], acc[mt][nt][1] * rs[1],
+                                                    acc[mt][nt][2] * rs[2], acc[mt][nt][3] * rs[3]};
+            } else {
+#pragma unroll
+              for (int r = 0; r < 4; ++r)
+                if (mr + r < M) vp[r] = acc[mt][nt][r] * rs[r];
+            }
+          }
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int mt = 0; mt < WM; ++mt) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 64 + mt * 16 + 4 * g + r;
+      const int m = m0 + wm * 16 * WM + mt * 16 + 4 * g + r;
       if (m >= M) continue;
       float rs = 1.f;
       if constexpr (PREC == P_I8) rs = a_scale[m];
       if constexpr (EPI == E_GEGLU) {
 #pragma unroll
-        for (int nt = 0; nt < 2; ++nt) {
-          const int n = nb * 64 + wn * 32 + nt * 16 + li;
-          const float v = gelu_erf(acc[mt][nt][r] * rs) * (acc[mt][nt + 2][r] * rs);
+        for (int nt = 0; nt < WN / 2; ++nt) {
+          const int n = nb * (BN / 2) + wn * (BN / 4) + nt * 16 + li;
+          const float v = gelu_erf(acc[mt][nt][r] * rs) * (acc[mt][nt + WN / 2][r] * rs);
           if constexpr (OUT == O_BF16) reinterpret_cast<uint16_t*>(C)[(size_t)m * N + n] = f32_to_bf16(v);
           else reinterpret_cast<float*>(C)[(size_t)m * N + n] = v;
         }
       } else {
 #pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int n = nb * BN + wn * 64 + nt * 16 + li;
+        for (int nt = 0; nt < WN; ++nt) {
+          const int n = nb * BN + wn * 16 * WN + nt * 16 + li;
           const float v = acc[mt][nt][r] * rs;
           if constexpr (EPI == E_RESID) {
             reinterpret_cast<float*>(C)[(size_t)m * N + n] += v;
@@ -230,26 +349,34 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
   }
 }
 
-template <int PREC, int EPI, int OUT>
+template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES = 4>
 void go(const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N, int K, void* C,
-        hipStream_t s) {
-  const int nblocks = EPI == E_GEGLU ? N / 64 : N / BN;
-  const dim3 grid(nblocks, (M + BM - 1) / BM);
-  k_gemm<PREC, EPI, OUT><<<grid, 256, 0, s>>>(reinterpret_cast<const uint8_t*>(A), a_scale,
-                                               reinterpret_cast<const uint8_t*>(W), w_scale, C, M, N, K);
+        hipStream_t s, const QkvOut& qo = QkvOut{}) {
+  using G = Cfg<WM, WN, PREC, STAGES>;
+  static bool attr_set = false;  // once per instantiation
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<PREC, EPI, OUT, WM, WN, STAGES>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
+    attr_set = true;
+  }
+  const int n_blocks = EPI == E_GEGLU ? N / (G::BN / 2) : N / G::BN;
+  const int m_blocks = (M + G::BM - 1) / G::BM;
+  k_gemm<PREC, EPI, OUT, WM, WN, STAGES><<<n_blocks * m_blocks, 256, G::LDS, s>>>(reinterpret_cast<const uint8_t*>(A), a_scale,
+                                                 reinterpret_cast<const uint8_t*>(W), w_scale, C, M, N, K, n_blocks,
+                                                 m_blocks, qo);
 }
 
-template <int PREC>
+template <int PREC, int WM, int ST>
 void go_prec(int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N, int K,
              void* C, int out_kind, hipStream_t s) {
   if (epi == E_RESID) {
-    go<PREC, E_RESID, O_F32>(A, a_scale, W, w_scale, M, N, K, C, s);
+    go<PREC, E_RESID, O_F32, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
   } else if (epi == E_GEGLU) {
-    if (out_kind == O_BF16) go<PREC, E_GEGLU, O_BF16>(A, a_scale, W, w_scale, M, N, K, C, s);
-    else go<PREC, E_GEGLU, O_F32>(A, a_scale, W, w_scale, M, N, K, C, s);
+    if (out_kind == O_BF16) go<PREC, E_GEGLU, O_BF16, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
+    else go<PREC, E_GEGLU, O_F32, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
   } else {
-    if (out_kind == O_BF16) go<PREC, E_STORE, O_BF16>(A, a_scale, W, w_scale, M, N, K, C, s);
-    else go<PREC, E_STORE, O_F32>(A, a_scale, W, w_scale, M, N, K, C, s);
+    if (out_kind == O_BF16) go<PREC, E_STORE, O_BF16, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
+    else go<PREC, E_STORE, O_F32, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
   }
 }
 
@@ -258,9 +385,34 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
 void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
                  int N, int K, void* C, int out_kind, hipStream_t s) {
   if (M <= 0) return;
-  if (prec == P_F32) go_prec<P_F32>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
-  else if (prec == P_BF16) go_prec<P_BF16>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
-  else go_prec<P_I8>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+  // 64 x 128 tiles double-buffered (48 KB of LDS: three blocks share a CU
+  // and overlap one another's pipeline fill and epilogue); a third stage for
+  // long K.  Measured on MI355X against 128 x 128 tiles and 2 to 4 stages.
+  const bool long_k = K > 1024;
+  if (prec == P_F32) {
+    if (long_k) go_prec<P_F32, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+    else go_prec<P_F32, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+  } else if (prec == P_BF16) {
+    if (long_k) go_prec<P_BF16, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+    else go_prec<P_BF16, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+  } else {
+    if (long_k) go_prec<P_I8, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+    else go_prec<P_I8, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+  }
+}
+
+void launch_gemm_qkv(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int K,
+                     void* qkv, int out_kind, const QkvOut& qo, hipStream_t s) {
+  if (M <= 0) return;
+  const int N = 3 * qo.hidden;
+  if (prec == P_F32) {
+    go<P_F32, E_QKV, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+  } else if (prec == P_BF16) {
+    if (out_kind == O_BF16) go<P_BF16, E_QKV, O_BF16, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+    else go<P_BF16, E_QKV, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+  } else {
+    go<P_I8, E_QKV, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+  }
 }
 
 }  // namespace tte

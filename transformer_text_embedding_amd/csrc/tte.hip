@@ -33,8 +33,9 @@ tte_status fail(tte_status s, const std::string& msg) {
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t x, xa, ascale, qkv, o, y, seg, off, unit, partial, cosg, sing, cosl, sinl, total;
+  size_t x, xa, ascale, qkv, vt, o, y, seg, off, unit, partial, cosg, sing, cosl, sinl, total;
   int max_units;
+  int vt_stride;
 };
 
 int act_bytes(int prec) { return prec == TTE_BF16 ? 2 : 4; }
@@ -54,6 +55,10 @@ Layout layout_of(const tte_config& c) {
   L.xa = take(c.precision == TTE_INT8 ? T * (H > I ? H : I) : T * H * ab);
   L.ascale = take(T * 4);
   L.qkv = take(T * 3 * H * ab);
+  // V transposed, [H][vt_stride]: 64 tokens of slack so a key tile that
+  // starts at the last token stays inside the buffer
+  L.vt_stride = (int)((T + 64 + 7) / 8 * 8);
+  L.vt = take(H * (size_t)L.vt_stride * ab);
   L.o = take(T * H * ab);
   L.y = take(T * I * ab);
   L.seg = take(T * sizeof(Seg));
@@ -126,6 +131,7 @@ struct tte_model {
   void* xa;
   float* ascale;
   void* qkv;
+  void* vt;
   void* o;
   void* y;
   Seg* seg;
@@ -263,12 +269,13 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
     }
     {
       ProfScope ps(m, TTE_K_GEMM_QKV, s);
-      launch_gemm(P, E_STORE, a_in, m->ascale, LW.wqkv, LW.wqkv_scale, T, 3 * H, H, m->qkv, act, s);
+      const QkvOut qo{m->seg, glob ? m->cosg : m->cosl, glob ? m->sing : m->sinl, m->vt, m->L.vt_stride, H};
+      launch_gemm_qkv(P, a_in, m->ascale, LW.wqkv, LW.wqkv_scale, T, H, m->qkv, act, qo, s);
     }
     {
       ProfScope ps(m, glob ? TTE_K_ATTN_GLOBAL : TTE_K_ATTN_LOCAL, s);
-      launch_attention(P == TTE_BF16 ? P_BF16 : P_F32, m->qkv, m->o, m->seg, glob ? m->cosg : m->cosl,
-                       glob ? m->sing : m->sinl, T, nh, glob, c.window, s);
+      launch_attention(P == TTE_BF16 ? P_BF16 : P_F32, m->qkv, m->vt, m->L.vt_stride, m->o, m->seg, T, nh, glob,
+                       c.window, s);
     }
     const void* o_in = m->o;
     if (P == TTE_INT8) {
@@ -368,6 +375,7 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   m->xa = b + L.xa;
   m->ascale = reinterpret_cast<float*>(b + L.ascale);
   m->qkv = b + L.qkv;
+  m->vt = b + L.vt;
   m->o = b + L.o;
   m->y = b + L.y;
   m->seg = reinterpret_cast<Seg*>(b + L.seg);
@@ -395,6 +403,10 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   const size_t dst[4] = {L.cosg, L.sing, L.cosl, L.sinl};
   for (int i = 0; i < 4 && st == TTE_OK; ++i)
     st = hip_check(hipMemcpy(b + dst[i], tab.data() + i * n, n * 4, hipMemcpyHostToDevice), "hipMemcpy(rope)");
+  // the slack columns of V^T are read (and multiplied by zero weights) by
+  // key tiles that run past the pack: keep them finite
+  if (st == TTE_OK)
+    st = hip_check(hipMemset(m->vt, 0, (size_t)c.hidden * L.vt_stride * act_bytes(c.precision)), "hipMemset(vt)");
   if (st == TTE_OK)
     st = hip_check(hipHostMalloc((void**)&m->h_stage, sizeof(int) * 2 * ((size_t)c.max_texts + 1) * STAGE_SLOTS,
                                  hipHostMallocDefault),
@@ -493,8 +505,37 @@ tte_status tte_op_attention(tte_model* m, int32_t layer, const void* d_qkv, int3
   if (st != TTE_OK) return st;
   k_seg<<<(n_tokens + 255) / 256, 256, 0, s>>>(m->d_off, n_texts, n_tokens, m->seg);
   const int glob = (layer % m->cfg.global_every) == 0;
-  launch_attention(m->cfg.precision == TTE_BF16 ? P_BF16 : P_F32, d_qkv, d_o, m->seg, glob ? m->cosg : m->cosl,
-                   glob ? m->sing : m->sinl, n_tokens, m->cfg.n_heads, glob, m->cfg.window, s);
+  const int prec = m->cfg.precision == TTE_BF16 ? P_BF16 : P_F32;
+  const QkvOut qo{m->seg, glob ? m->cosg : m->cosl, glob ? m->sing : m->sinl, m->vt, m->L.vt_stride, m->cfg.hidden};
+  launch_qkv_prep(prec, d_qkv, m->qkv, qo, n_tokens, s);
+  launch_attention(prec, m->qkv, m->vt, m->L.vt_stride, d_o, m->seg, n_tokens, m->cfg.n_heads, glob, m->cfg.window, s);
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+tte_status tte_op_qkv(tte_model* m, int32_t layer, const void* d_a, const float* d_a_scale, int32_t n_tokens,
+                      const int32_t* h_offsets, int32_t n_texts, void* d_qk, void* d_vt, void* stream) {
+  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+  if (layer < 0 || layer >= m->cfg.n_layers) return fail(TTE_E_INVALID, "layer out of range");
+  tte_status st = check_pack(m->cfg, n_tokens, h_offsets, n_texts);
+  if (st != TTE_OK) return st;
+  if (n_texts == 0) return TTE_OK;
+  if (!d_a || !d_qk || !d_vt || (m->cfg.precision == TTE_INT8 && !d_a_scale)) return fail(TTE_E_INVALID, "NULL buffer");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  int n_units = 0;
+  st = upload_pack(m, h_offsets, n_texts, &n_units, s);
+  if (st != TTE_OK) return st;
+  k_seg<<<(n_tokens + 255) / 256, 256, 0, s>>>(m->d_off, n_texts, n_tokens, m->seg);
+  const int glob = (layer % m->cfg.global_every) == 0;
+  const int H = m->cfg.hidden, P = m->cfg.precision;
+  const tte_layer_weights& LW = m->layers[layer];
+  const QkvOut qo{m->seg, glob ? m->cosg : m->cosl, glob ? m->sing : m->sinl, m->vt, m->L.vt_stride, H};
+  launch_gemm_qkv(P, d_a, d_a_scale, LW.wqkv, LW.wqkv_scale, n_tokens, H, d_qk, P == TTE_BF16 ? O_BF16 : O_F32, qo, s);
+  const size_t es = P == TTE_BF16 ? 2 : 4;
+  st = hip_check(hipMemcpy2DAsync(d_vt, (size_t)n_tokens * es, m->vt, (size_t)m->L.vt_stride * es, (size_t)n_tokens * es,
+                                  (size_t)H, hipMemcpyDeviceToDevice, s),
+                 "hipMemcpy2DAsync(vt)");
+  if (st != TTE_OK) return st;
   return hip_check(hipGetLastError(), "kernel launch");
 }
 
