@@ -157,7 +157,7 @@ def main():
     breakdown = None
     if a.breakdown:
         h = models[0].handle
-        B.tte_profile_start(h, (1 << B.TTE_K_COUNT) - 1, 200 * len(packs) + 16)
+        B.tte_profile_start(h, (1 << B.TTE_K_COUNT) - 1, (10 * cfg.layers + 4) * len(packs) + 16)
         step(1)
         prof = B.tte_profile_stop(h)
         breakdown = {}
