@@ -37,6 +37,20 @@ GEMM_CLASSES = {"gemm_qkv": lambda H, I: 2 * 3 * H * H, "gemm_o": lambda H, I: 2
                 "gemm_geglu": lambda H, I: 2 * 2 * I * H, "gemm_o2": lambda H, I: 2 * H * I}
 
 
+def traffic_from_profile(kernel_source: str, profile: str):
+    """HBM bytes per launch of the dominant kernel from the committed counter
+    summary, or None if the kernel source changed since it was taken."""
+    import hashlib
+    try:
+        meta = json.load(open(profile))
+        src = open(kernel_source, "rb").read()
+    except OSError:
+        return None
+    if hashlib.sha256(src).hexdigest()[:16] != meta.get("source_sha256_16"):
+        return None
+    return meta["per_launch_mean"]["traffic_bytes"]
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -73,6 +87,8 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-launch events of the dominant kernel")
     ap.add_argument("--breakdown", action="store_true", help="add an untimed step timing every kernel class")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized fp32 buffer 5 times with torch (known bytes, for HBM counter scaling)")
     a = ap.parse_args()
     if a.gpus != 1:
         print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
@@ -88,6 +104,15 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     dev = torch.device("cuda:0")
+    if a.copy_calibration:
+        n = a.copy_calibration * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "copies": 5}), flush=True)
+        return
     spec = ti.workload(a.workload)
     cfg = spec["cfg"]
     t0 = time.perf_counter()
@@ -149,8 +174,13 @@ def main():
         flops = GEMM_CLASSES[dominant](H, I) * tokens_per_step * cfg.layers * a.steps
         achieved = flops / (ms_dom / 1e3) / 1e12
         peak = PEAK_TFLOPS[cfg.precision]
+        traffic = None
+        if a.workload == "full_bf16_packs2048":
+            traffic = traffic_from_profile(
+                os.path.join(ROOT, "transformer_text_embedding_amd", "csrc", "kernels_gemm.hip"),
+                os.path.join(ROOT, "profiles", "traffic_gemm_geglu_full_bf16_packs2048.json"))
         roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4), "traffic": None, "kernel": f"k_gemm ({dominant})",
+                    "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": f"k_gemm ({dominant})",
                     "launches": int(n_dom), "avg_launch_us": round(ms_dom * 1e3 / max(n_dom, 1), 2),
                     "flops_per_launch_avg": int(flops / max(n_dom, 1)), "measured_in": "single-stream pass"}
 

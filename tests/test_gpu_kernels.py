@@ -77,8 +77,10 @@ def test_layernorm_to_int8_codes():
 # GEMMs
 # --------------------------------------------------------------------------
 
-SHAPES = [(178, 384, 128), (957, 2304, 768), (300, 768, 3072), (130, 512, 256), (1, 128, 128)]
-GEGLU_SHAPES = [(178, 256, 128), (957, 3072, 768), (65, 64, 256)]
+# tile configurations: 32x128 (few narrow tiles), 64x128, 64x128 with 3
+# stages (K > 1024), 128x128 (>= 1024 tiles of 128x128)
+SHAPES = [(178, 384, 128), (957, 2304, 768), (300, 768, 3072), (130, 512, 256), (1, 128, 128), (4100, 4096, 128)]
+GEGLU_SHAPES = [(178, 256, 128), (957, 3072, 768), (65, 64, 256), (2100, 4096, 128)]
 
 
 def _run_gemm(prec, epi, a, a_s, w, w_s, M, N, K, c, out_kind):

@@ -22,8 +22,10 @@
 //    r stored at slot chunk ^ (r & 7): the 8 lanes of a fragment read (rows
 //    r..r+7, one chunk) then hit 8 distinct bank groups.
 //  * Blocks are ordered so that the blocks one XCD runs (block id mod 8)
-//    form a contiguous run of the n-major tile order: they share W columns,
-//    which then stay in that XCD's L2.
+//    form a contiguous run of a grouped tile order covering about half of
+//    A's rows and a quarter of W's rows, a working set that fits the XCD's
+//    4 MB L2 (measured: HBM/MALL fetches fell from 3.4x the operand bytes
+//    with a plain n-major order).
 //
 //   fp32: v_mfma_f32_16x16x4_f32, 4 per 16-k chunk (each lane reads a float4
 //         and feeds one element per MFMA; A and W use the same k order).
@@ -137,12 +139,18 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
   const int g = lane >> 4, li = lane & 15;
 
   // XCD-aware tile order: block b runs on XCD b mod 8; XCD x gets a
-  // contiguous run of the n-major tile order.
+  // contiguous run of a grouped order (groups of n_blocks/4 column
+  // blocks, every row block inside a group).  A run of n_tiles/8 tiles then
+  // spans about half of A's rows and a quarter of W's, which together fit
+  // that XCD's L2.
   const int n_tiles = n_blocks * m_blocks;
   const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int per = n_tiles >> 3, extra = n_tiles & 7;
   const int tile = xcd * per + min(xcd, extra) + local;
-  const int nb = tile / m_blocks, mb = tile % m_blocks;
+  const int grp = max(1, n_blocks >> 2);
+  const int ng = tile / (m_blocks * grp), gbase = ng * grp, gwidth = min(grp, n_blocks - gbase);
+  const int grem = tile - ng * m_blocks * grp;
+  const int mb = grem / gwidth, nb = gbase + grem % gwidth;
   const int m0 = mb * BM;
   const size_t row_bytes = (size_t)K * F::ES;
   const int nk = K / F::BK;
@@ -380,39 +388,56 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
   }
 }
 
+// Tile choice, measured on MI355X (bf16, the encoder's shapes at 1.9k and
+// 16k tokens): 128 x 128 once there are >= 1024 such tiles; else 32 x 128
+// for narrow, short-K products with few tiles (the 768-wide attention
+// output of a ~2k-token pack); else
+// 64 x 128, with a third stage for long K.
+enum TileCfg { T32, T64, T64L, T128 };
+
+TileCfg pick_tiles(int M, int n_cols, int K) {
+  const long tiles128 = (long)((M + 127) / 128) * (n_cols / 128);
+  if (tiles128 >= 1024) return T128;
+  if (tiles128 < 256 && n_cols <= 1024 && K <= 1024) return T32;
+  return K > 1024 ? T64L : T64;
+}
+
+template <int PREC>
+void launch_prec(int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N,
+                 int K, void* C, int out_kind, hipStream_t s) {
+  switch (pick_tiles(M, epi == E_GEGLU ? 2 * N : N, K)) {
+    case T128: go_prec<PREC, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
+    case T32: go_prec<PREC, 1, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
+    case T64L: go_prec<PREC, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
+    default: go_prec<PREC, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
+  }
+}
+
+template <int PREC, int OUT>
+void launch_qkv_prec(const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int K,
+                     void* qkv, const QkvOut& qo, hipStream_t s) {
+  const int N = 3 * qo.hidden;
+  if (pick_tiles(M, N, K) == T128) go<PREC, E_QKV, OUT, 4, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+  else go<PREC, E_QKV, OUT, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+}
+
 }  // namespace
 
 void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
                  int N, int K, void* C, int out_kind, hipStream_t s) {
   if (M <= 0) return;
-  // 64 x 128 tiles double-buffered (48 KB of LDS: three blocks share a CU
-  // and overlap one another's pipeline fill and epilogue); a third stage for
-  // long K.  Measured on MI355X against 128 x 128 tiles and 2 to 4 stages.
-  const bool long_k = K > 1024;
-  if (prec == P_F32) {
-    if (long_k) go_prec<P_F32, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
-    else go_prec<P_F32, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
-  } else if (prec == P_BF16) {
-    if (long_k) go_prec<P_BF16, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
-    else go_prec<P_BF16, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
-  } else {
-    if (long_k) go_prec<P_I8, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
-    else go_prec<P_I8, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
-  }
+  if (prec == P_F32) launch_prec<P_F32>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+  else if (prec == P_BF16) launch_prec<P_BF16>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+  else launch_prec<P_I8>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
 }
 
 void launch_gemm_qkv(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int K,
                      void* qkv, int out_kind, const QkvOut& qo, hipStream_t s) {
   if (M <= 0) return;
-  const int N = 3 * qo.hidden;
-  if (prec == P_F32) {
-    go<P_F32, E_QKV, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
-  } else if (prec == P_BF16) {
-    if (out_kind == O_BF16) go<P_BF16, E_QKV, O_BF16, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
-    else go<P_BF16, E_QKV, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
-  } else {
-    go<P_I8, E_QKV, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
-  }
+  if (prec == P_F32) launch_qkv_prec<P_F32, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
+  else if (prec == P_BF16 && out_kind == O_BF16) launch_qkv_prec<P_BF16, O_BF16>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
+  else if (prec == P_BF16) launch_qkv_prec<P_BF16, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
+  else launch_qkv_prec<P_I8, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
 }
 
 }  // namespace tte
