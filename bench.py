@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--workload", default="full_bf16_packs2048")
     ap.add_argument("--streams", type=int, default=3,
                     help="concurrent streams, one model each (3 measured best with 4 hardware queues per process)")
+    ap.add_argument("--split-k", action="store_true",
+                    help="TTE_FLAG_SPLIT_K: split the down-projection of short packs (lower single-call latency)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -122,9 +124,10 @@ def main():
         f"{sum(p.n_tokens for p in packs)} tokens")
     max_tokens = max(p.n_tokens for p in packs)
     S = max(1, a.streams)
-    model = Model(cfg, w, max_tokens=max_tokens, max_text_len=max(max_tokens, 512), max_texts=1024, device="cuda:0")
+    model = Model(cfg, w, max_tokens=max_tokens, max_text_len=max(max_tokens, 512), max_texts=1024, device="cuda:0",
+                  split_k=a.split_k)
     models = [model] + [Model(cfg, None, max_tokens=max_tokens, max_text_len=max(max_tokens, 512), max_texts=1024,
-                              device="cuda:0", shared_from=model) for _ in range(S - 1)]
+                              device="cuda:0", shared_from=model, split_k=a.split_k) for _ in range(S - 1)]
     streams = [torch.cuda.Stream(device=dev) for _ in range(S)]
     ids = [torch.from_numpy(p.ids).to(dev) for p in packs]
     outs = [torch.empty((p.n_texts, cfg.hidden), dtype=torch.float32, device=dev) for p in packs]
@@ -208,7 +211,7 @@ def main():
         "config": {"workload": a.workload, "packs_per_step": len(packs), "tokens_per_step": tokens_per_step,
                    "pack_budget": spec.get("pack_budget"), "layers": cfg.layers, "hidden": cfg.hidden,
                    "heads": cfg.heads, "intermediate": cfg.intermediate, "calls_per_step": len(packs),
-                   "streams": S, "single_stream_ms_per_step": round(single_ms, 3) if single_ms else None},
+                   "streams": S, "split_k": a.split_k, "single_stream_ms_per_step": round(single_ms, 3) if single_ms else None},
         "roofline": roofline,
     }
     if breakdown is not None:

@@ -56,6 +56,18 @@ typedef enum {
                    block; attention, norms and residual in fp32 */
 } tte_precision;
 
+/* Execution options (tte_config.flags). */
+typedef enum {
+  /* Split the down-projection (I -> H) of short packs over K into two
+   * partial products, summed into the residual stream by the next norm
+   * kernel.  A 768-wide output of a ~2k-token pack makes fewer tiles than
+   * the chip has compute units; splitting doubles them and shortens one
+   * call by about 5%.  It costs 2 * max_tokens * H * 4 bytes of workspace
+   * and extra HBM traffic, which lowers throughput when several calls
+   * already share the GPU on concurrent streams, so it is off by default. */
+  TTE_FLAG_SPLIT_K = 1
+} tte_flag;
+
 /* Model shape and limits.  Defaults in parentheses are the page's values. */
 typedef struct {
   int32_t vocab;
@@ -73,6 +85,7 @@ typedef struct {
   int32_t max_text_len;     /* longest text (RoPE tables are sized by it) */
   int32_t max_texts;        /* largest n_texts of one call */
   int32_t precision;        /* tte_precision */
+  int32_t flags;            /* OR of tte_flag values (0) */
 } tte_config;
 
 /* Device pointers to one layer's weights, in the storage format of the
@@ -175,6 +188,22 @@ typedef enum { TTE_EPI_STORE = 0, TTE_EPI_RESIDUAL = 1, TTE_EPI_GEGLU = 2 } tte_
 tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, const float* d_a_scale,
                        const void* d_w, const float* d_w_scale, int32_t M, int32_t N, int32_t K,
                        void* d_c, int32_t out_kind, void* stream);
+
+/* Split-K form of the same product for the residual projections: K is cut
+ * into `splits` equal parts (each a multiple of 128 bytes of an operand
+ * row) and part s writes its fp32 product to d_partials + s * M * N
+ * (int8: already multiplied by both scales). */
+tte_status tte_op_gemm_splitk(int32_t precision, const void* d_a, const float* d_a_scale, const void* d_w,
+                              const float* d_w_scale, int32_t M, int32_t N, int32_t K, int32_t splits,
+                              float* d_partials, void* stream);
+
+/* Residual update from split-K partials fused with the next norm: d_x fp32
+ * [rows, width] += d_partials[0] + ... + d_partials[splits-1] (in that
+ * order, each [rows, width]), written back; then, as tte_op_layernorm, the
+ * updated rows are normalised (d_gamma non-null) or converted into d_out;
+ * out_kind = -1 writes no output. */
+tte_status tte_op_resid_ln(float* d_x, const float* d_partials, int32_t splits, const float* d_gamma, int32_t rows,
+                           int32_t width, float eps, int32_t out_kind, void* d_out, float* d_scale, void* stream);
 
 /* Attention of layer `layer` of model m over the pack described by
  * h_offsets: d_qkv [n_tokens, 3H] (fp32, or bf16 in TTE_BF16) -> d_o

@@ -41,9 +41,15 @@ def test_workspace_size_grows_with_limits(lib):
     assert a % 256 == 0
 
 
+def test_split_k_flag_adds_partials_workspace(lib):
+    a = B.tte_workspace_size(_cfg())
+    b = B.tte_workspace_size(_cfg(flags=B.TTE_FLAG_SPLIT_K))
+    assert b - a == 2 * 2048 * 768 * 4  # two fp32 partial products [max_tokens, H]
+
+
 @pytest.mark.parametrize("field,value", [
     ("head_dim", 32), ("hidden", 700), ("intermediate", 3000), ("precision", 7), ("max_tokens", 0),
-    ("global_every", 0), ("window", -1), ("ln_eps", 0.0), ("n_layers", 0), ("max_texts", 0)])
+    ("global_every", 0), ("window", -1), ("ln_eps", 0.0), ("n_layers", 0), ("max_texts", 0), ("flags", 2)])
 def test_bad_configs_rejected(lib, field, value):
     c = _cfg(**{field: value})
     n = ctypes.c_size_t(0)
@@ -88,6 +94,13 @@ def test_op_gemm_shape_checks_need_no_gpu(lib):
     st = lib.tte_op_gemm(B.TTE_BF16, B.TTE_EPI_STORE, None, None, None, None, 16, 128, 96, None, 0, None)
     assert st == B.TTE_E_UNSUPPORTED
     st = lib.tte_op_gemm(B.TTE_INT8, B.TTE_EPI_RESIDUAL, None, None, None, None, 16, 128, 128, None, 1, None)
+    assert st == B.TTE_E_INVALID
+    # split-K: K must divide into parts of whole 128-byte chunks
+    st = lib.tte_op_gemm_splitk(B.TTE_BF16, None, None, None, None, 16, 128, 320, 2, None, None)
+    assert st == B.TTE_E_UNSUPPORTED
+    st = lib.tte_op_gemm_splitk(B.TTE_BF16, None, None, None, None, 16, 128, 512, 0, None, None)
+    assert st == B.TTE_E_INVALID
+    st = lib.tte_op_resid_ln(None, None, 1, None, 4, 768, 1e-5, 3, None, None, None)
     assert st == B.TTE_E_INVALID
 
 

@@ -162,25 +162,29 @@ def _golden(name, pack_index):
     return cfg, w, pack, texts, emb
 
 
-FULL_CASES = [("full_fp32_957", 0), ("full_bf16_packs2048", 0), ("full_bf16_packs2048", 1),
-              ("full_int8_packs2048", 0), ("full_int8_packs2048", 1), ("full_bf16_4x4096", 0)]
+# (workload, pack, split_k): TTE_FLAG_SPLIT_K changes the down-projection
+# of the ~2k-token packs (the 16k-token packs stay unsplit)
+FULL_CASES = [("full_fp32_957", 0, False), ("full_bf16_packs2048", 0, False), ("full_bf16_packs2048", 1, False),
+              ("full_int8_packs2048", 0, False), ("full_int8_packs2048", 1, False), ("full_bf16_4x4096", 0, False),
+              ("full_fp32_957", 0, True), ("full_bf16_packs2048", 1, True), ("full_int8_packs2048", 0, True)]
 
 
 @pytest.fixture(scope="module")
 def full_models():
     cache = {}
 
-    def get(name):
-        if name not in cache:
+    def get(name, split_k=False):
+        key = (name, split_k)
+        if key not in cache:
             for k in list(cache):
                 cache.pop(k).close()
             cfg = ti.workload(name)["cfg"]
             w = ti.cached_storage_weights(cfg)
             packs = ti.make_packs(name)
             max_tokens = max(p.n_tokens for p in packs)
-            cache[name] = Model(cfg, w, max_tokens=max_tokens, max_text_len=max(4096, max_tokens),
-                                max_texts=256)
-        return cache[name]
+            cache[key] = Model(cfg, w, max_tokens=max_tokens, max_text_len=max(4096, max_tokens),
+                               max_texts=256, split_k=split_k)
+        return cache[key]
 
     yield get
     for m in cache.values():
@@ -188,11 +192,11 @@ def full_models():
 
 
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,pack_index", FULL_CASES)
-def test_full_size_matches_oracle(full_models, name, pack_index):
-    say(f"{name} pack {pack_index}")
+@pytest.mark.parametrize("name,pack_index,split_k", FULL_CASES)
+def test_full_size_matches_oracle(full_models, name, pack_index, split_k):
+    say(f"{name} pack {pack_index} split_k {split_k}")
     cfg, w, pack, texts, ref = _golden(name, pack_index)
-    m = full_models(name)
+    m = full_models(name, split_k)
     got = host(m.embed_pack(dev(pack.ids), pack.offsets))
     np.testing.assert_allclose(np.linalg.norm(got, axis=1), 1.0, atol=1e-5)
     if texts is not None:
@@ -201,15 +205,17 @@ def test_full_size_matches_oracle(full_models, name, pack_index):
     say(f"  T={pack.n_tokens} B={pack.n_texts} cos min {cos.min():.7f} max|d| {np.abs(got - ref).max():.2e}")
 
 
-@pytest.mark.parametrize("name", ["full_fp32_957", "full_bf16_packs2048", "full_int8_packs2048"])
-def test_full_size_first_layers_trace(full_models, name):
+@pytest.mark.parametrize("name,split_k", [("full_fp32_957", False), ("full_bf16_packs2048", False),
+                                          ("full_int8_packs2048", False), ("full_fp32_957", True),
+                                          ("full_bf16_packs2048", True)])
+def test_full_size_first_layers_trace(full_models, name, split_k):
     """Residual stream after the embedding norm and the first two layers
     (one global, one local) of the full-size model, per token, against the
     oracle's fp64 states."""
     cfg = ti.workload(name)["cfg"]
     w = ti.cached_storage_weights(cfg)
     pack = ti.make_packs(name)[0]
-    m = full_models(name)
+    m = full_models(name, split_k)
     states, _ = m.trace(dev(pack.ids), pack.offsets, 2)
     got = host(states)
     ref = oracle.encode_layers(cfg.as_dict(), w, pack.ids, pack.offsets, n_layers=2)

@@ -206,6 +206,102 @@ def test_gemm_int8_scaled(M, N, K):
         np.testing.assert_allclose(host(cg), oracle.geglu(ref), atol=4e-6 * scale * scale + 1e-6, rtol=1e-4)
 
 
+# split-K residual projection: (M, N, K, splits); 2 or 3 stages per part
+SPLIT_SHAPES = [(957, 768, 3072, 2), (1913, 768, 3072, 4), (178, 384, 256, 2), (65, 256, 1536, 3), (1, 128, 512, 2)]
+
+
+def _split_operands(prec, M, N, K, rng):
+    """Device operands and fp64 per-part references of the split product."""
+    if prec == "int8":
+        x = rng.normal(size=(M, K)).astype(np.float32)
+        qx, sx = oracle.quantize_rows_7bit(x)
+        qw, sw = ti.quantize_weight_blocks(rng.normal(0, 0.02, size=(N, K)).astype(np.float32))
+        return (B.TTE_INT8, dev(qx), dev(sx), dev(qw), dev(sw),
+                lambda k0, k1: oracle.block_matmul_int8(qx[:, k0:k1], sx, qw[:, k0:k1], sw[:, k0 // 32:k1 // 32]))
+    a = rng.normal(size=(M, K)).astype(np.float32)
+    w = rng.normal(0, 0.02, size=(N, K)).astype(np.float32)
+    if prec == "bf16":
+        ab, wb = ti.bf16_bits(a), ti.bf16_bits(w)
+        av, wv = ti.bf16_to_f32(ab).astype(np.float64), ti.bf16_to_f32(wb).astype(np.float64)
+        return B.TTE_BF16, dev(ab), None, dev(wb), None, lambda k0, k1: av[:, k0:k1] @ wv[:, k0:k1].T
+    av, wv = a.astype(np.float64), w.astype(np.float64)
+    return B.TTE_FP32, dev(a), None, dev(w), None, lambda k0, k1: av[:, k0:k1] @ wv[:, k0:k1].T
+
+
+@pytest.mark.parametrize("M,N,K,splits", SPLIT_SHAPES)
+@pytest.mark.parametrize("prec", ["fp32", "bf16", "int8"])
+def test_gemm_splitk_partials(M, N, K, splits, prec):
+    t = torch()
+    say(f"gemm split-K {prec} {M}x{N}x{K} / {splits}")
+    rng = np.random.default_rng(13 * M + N + K + splits)
+    p, da, das, dw, dws, part_ref = _split_operands(prec, M, N, K, rng)
+    c = empty((splits, M, N), t.float32)
+    B.tte_op_gemm_splitk(p, da.data_ptr(), das.data_ptr() if das is not None else 0, dw.data_ptr(),
+                         dws.data_ptr() if dws is not None else 0, M, N, K, splits, c.data_ptr(), stream())
+    got = host(c)
+    kp = K // splits
+    for s in range(splits):
+        ref = part_ref(s * kp, (s + 1) * kp)
+        np.testing.assert_allclose(got[s], ref, atol=2e-5 * max(1.0, np.abs(ref).max()), rtol=1e-5)
+
+
+@pytest.mark.parametrize("M,N,K,splits", [(300, 256, 1024, 2), (64, 128, 768, 3)])
+def test_gemm_splitk_int8_bit_exact(M, N, K, splits):
+    """Scales 1: every partial is its exact integer sum."""
+    t = torch()
+    rng = np.random.default_rng(17 * M + K)
+    qx = rng.integers(-63, 64, size=(M, K)).astype(np.int8)
+    qw = rng.integers(-127, 128, size=(N, K)).astype(np.int8)
+    # device operands stay referenced until the kernel has run
+    dqx, dsx, dqw, dsw = dev(qx), dev(np.ones(M, np.float32)), dev(qw), dev(np.ones((N, K // 32), np.float32))
+    c = empty((splits, M, N), t.float32)
+    B.tte_op_gemm_splitk(B.TTE_INT8, dqx.data_ptr(), dsx.data_ptr(), dqw.data_ptr(), dsw.data_ptr(), M, N, K, splits,
+                         c.data_ptr(), stream())
+    got = host(c)
+    kp = K // splits
+    for s in range(splits):
+        exact = qx[:, s * kp:(s + 1) * kp].astype(np.int64) @ qw[:, s * kp:(s + 1) * kp].astype(np.int64).T
+        assert np.array_equal(got[s].astype(np.int64), exact) and np.all(got[s] == exact.astype(np.float32))
+
+
+@pytest.mark.parametrize("width,rows,splits", [(768, 357, 2), (768, 1, 4), (3072, 65, 1), (768, 100, 0)])
+def test_resid_ln(width, rows, splits):
+    """x += sum of partials, then LayerNorm / conversion / 7-bit codes."""
+    t = torch()
+    rng = np.random.default_rng(31 * width + rows + splits)
+    x = (rng.normal(size=(rows, width)) * 2).astype(np.float32)
+    parts = rng.normal(size=(max(splits, 1), rows, width)).astype(np.float32)
+    g = (1 + rng.normal(0, 0.1, size=width)).astype(np.float32)
+    new_x = x.copy()
+    for s in range(splits):
+        new_x = new_x + parts[s]  # fp32, in split order, as the kernel adds
+    ref = oracle.layer_norm(new_x, g, 1e-5)
+    dp, dg = dev(parts), dev(g)
+    for kind in (B.TTE_OUT_F32, B.TTE_OUT_BF16, B.TTE_OUT_I8, -1):
+        dx = dev(x)
+        out = empty((rows, width), {B.TTE_OUT_F32: t.float32, B.TTE_OUT_BF16: t.int16}.get(kind, t.int8))
+        sc = empty((rows,), t.float32)
+        B.tte_op_resid_ln(dx.data_ptr(), dp.data_ptr(), splits, dg.data_ptr(), rows, width, 1e-5, kind,
+                          out.data_ptr() if kind >= 0 else 0, sc.data_ptr() if kind == B.TTE_OUT_I8 else 0, stream())
+        np.testing.assert_array_equal(host(dx), new_x)
+        if kind == B.TTE_OUT_F32:
+            np.testing.assert_allclose(host(out), ref, atol=2e-5, rtol=0)
+        elif kind == B.TTE_OUT_BF16:
+            got_b = ti.bf16_to_f32(host(out).view(np.uint16)).astype(np.float64)
+            np.testing.assert_allclose(got_b, ref, rtol=2.0 ** -8, atol=1e-6)
+        elif kind == B.TTE_OUT_I8:
+            qr, sr = oracle.quantize_rows_7bit(ref)
+            diff = np.abs(host(out).astype(np.int64) - qr)
+            assert diff.max() <= 1 and np.mean(diff) < 1e-3
+            np.testing.assert_allclose(host(sc), sr, rtol=1e-5)
+    # no norm: plain conversion of the updated rows
+    dx = dev(x)
+    out = empty((rows, width), t.float32)
+    B.tte_op_resid_ln(dx.data_ptr(), dp.data_ptr(), splits, 0, rows, width, 1e-5, B.TTE_OUT_F32, out.data_ptr(), 0,
+                      stream())
+    np.testing.assert_array_equal(host(out), new_x)
+
+
 # --------------------------------------------------------------------------
 # attention
 # --------------------------------------------------------------------------

@@ -16,8 +16,11 @@ from . import binding as B
 __all__ = ["Model", "make_config", "B"]
 
 
-def make_config(spec, max_tokens: int, max_text_len: int, max_texts: Optional[int] = None) -> B.tte_config:
-    """tte_config from a dict / dataclass with the encoder's shape fields."""
+def make_config(spec, max_tokens: int, max_text_len: int, max_texts: Optional[int] = None,
+                split_k: bool = False) -> B.tte_config:
+    """tte_config from a dict / dataclass with the encoder's shape fields.
+    split_k sets TTE_FLAG_SPLIT_K (lower latency of one call on an idle GPU,
+    lower throughput under concurrent calls)."""
     d = spec if isinstance(spec, dict) else spec.as_dict()
     return B.tte_config(
         vocab=d["vocab"], hidden=d["hidden"], n_heads=d["heads"], head_dim=d["head_dim"],
@@ -26,7 +29,7 @@ def make_config(spec, max_tokens: int, max_text_len: int, max_texts: Optional[in
         rope_base_local=d.get("rope_base_local", 10000.0), ln_eps=d.get("ln_eps", 1e-5),
         max_tokens=max_tokens, max_text_len=max_text_len,
         max_texts=max_texts if max_texts is not None else max_tokens,
-        precision=B.PRECISIONS[d["precision"]])
+        precision=B.PRECISIONS[d["precision"]], flags=B.TTE_FLAG_SPLIT_K if split_k else 0)
 
 
 class Model:
@@ -38,13 +41,14 @@ class Model:
     """
 
     def __init__(self, spec, weights: dict, max_tokens: int = 2048, max_text_len: Optional[int] = None,
-                 max_texts: Optional[int] = None, device: str = "cuda:0", shared_from: "Model" = None):
+                 max_texts: Optional[int] = None, device: str = "cuda:0", shared_from: "Model" = None,
+                 split_k: bool = False):
         import torch
         self.torch = torch
         B.lib()
         self.device = torch.device(device)
         self.spec = spec if isinstance(spec, dict) else spec.as_dict()
-        self.cfg = make_config(self.spec, max_tokens, max_text_len or max_tokens, max_texts)
+        self.cfg = make_config(self.spec, max_tokens, max_text_len or max_tokens, max_texts, split_k)
         self.precision = self.spec["precision"]
         if shared_from is not None:
             self._keep = shared_from._keep

@@ -16,6 +16,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "tte.h")
 TTE_OK, TTE_E_INVALID, TTE_E_UNSUPPORTED, TTE_E_NOMEM, TTE_E_DEVICE = range(5)
 STATUS_NAMES = {0: "TTE_OK", 1: "TTE_E_INVALID", 2: "TTE_E_UNSUPPORTED", 3: "TTE_E_NOMEM", 4: "TTE_E_DEVICE"}
 TTE_FP32, TTE_BF16, TTE_INT8 = 0, 1, 2
+TTE_FLAG_SPLIT_K = 1
 PRECISIONS = {"fp32": TTE_FP32, "bf16": TTE_BF16, "int8": TTE_INT8}
 TTE_OUT_F32, TTE_OUT_BF16, TTE_OUT_I8 = 0, 1, 2
 TTE_EPI_STORE, TTE_EPI_RESIDUAL, TTE_EPI_GEGLU = 0, 1, 2
@@ -28,7 +29,8 @@ class tte_config(ctypes.Structure):
     _fields_ = [("vocab", c_int32), ("hidden", c_int32), ("n_heads", c_int32), ("head_dim", c_int32),
                 ("intermediate", c_int32), ("n_layers", c_int32), ("global_every", c_int32), ("window", c_int32),
                 ("rope_base_global", c_float), ("rope_base_local", c_float), ("ln_eps", c_float),
-                ("max_tokens", c_int32), ("max_text_len", c_int32), ("max_texts", c_int32), ("precision", c_int32)]
+                ("max_tokens", c_int32), ("max_text_len", c_int32), ("max_texts", c_int32), ("precision", c_int32),
+                ("flags", c_int32)]
 
 
 class tte_layer_weights(ctypes.Structure):
@@ -56,6 +58,10 @@ _SIGS = {
     "tte_op_quant7": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "tte_op_gemm": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                               c_void_p, c_int32, c_void_p]),
+    "tte_op_gemm_splitk": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
+                                     c_int32, c_void_p, c_void_p]),
+    "tte_op_resid_ln": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_float, c_int32, c_void_p,
+                                  c_void_p, c_void_p]),
     "tte_op_attention": (c_int32, [c_void_p, c_int32, c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p,
                                    c_void_p]),
     "tte_op_qkv": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p,
@@ -160,6 +166,21 @@ def tte_op_gemm(precision: int, epilogue: int, d_a: int, d_a_scale: int, d_w: in
     check(lib().tte_op_gemm(precision, epilogue, c_void_p(d_a), c_void_p(d_a_scale) if d_a_scale else None,
                             c_void_p(d_w), c_void_p(d_w_scale) if d_w_scale else None, M, N, K, c_void_p(d_c),
                             out_kind, c_void_p(stream)))
+
+
+def tte_op_gemm_splitk(precision: int, d_a: int, d_a_scale: int, d_w: int, d_w_scale: int, M: int, N: int, K: int,
+                       splits: int, d_partials: int, stream: int) -> None:
+    check(lib().tte_op_gemm_splitk(precision, c_void_p(d_a), c_void_p(d_a_scale) if d_a_scale else None, c_void_p(d_w),
+                                   c_void_p(d_w_scale) if d_w_scale else None, M, N, K, splits, c_void_p(d_partials),
+                                   c_void_p(stream)))
+
+
+def tte_op_resid_ln(d_x: int, d_partials: int, splits: int, d_gamma: int, rows: int, width: int, eps: float,
+                    out_kind: int, d_out: int, d_scale: int, stream: int) -> None:
+    check(lib().tte_op_resid_ln(c_void_p(d_x), c_void_p(d_partials) if d_partials else None, splits,
+                                c_void_p(d_gamma) if d_gamma else None, rows, width, eps, out_kind,
+                                c_void_p(d_out) if d_out else None, c_void_p(d_scale) if d_scale else None,
+                                c_void_p(stream)))
 
 
 def tte_op_attention(model: int, layer: int, d_qkv: int, n_tokens: int, offsets, d_o: int, stream: int) -> None:

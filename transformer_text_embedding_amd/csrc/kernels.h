@@ -10,7 +10,7 @@ namespace tte {
 
 enum Prec { P_F32 = 0, P_BF16 = 1, P_I8 = 2 };
 enum OutKind { O_F32 = 0, O_BF16 = 1, O_I8 = 2 };
-enum Epi { E_STORE = 0, E_RESID = 1, E_GEGLU = 2, E_QKV = 3 };
+enum Epi { E_STORE = 0, E_RESID = 1, E_GEGLU = 2, E_QKV = 3, E_PART = 4 };
 
 // Per-token text bounds: seg[t] = {offsets[b], offsets[b+1]} of t's text.
 struct Seg {
@@ -52,6 +52,20 @@ void launch_quant7(const float* x, int rows, int width, int8_t* q, float* scale,
 // (GEGLU: N % 64 == 0) and K % 128 == 0.
 void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const void* W, const float* w_scale,
                  int M, int N, int K, void* C, int out_kind, hipStream_t s);
+
+// Split-K product for the residual projections: the K range is cut into
+// `splits` equal parts (K % (128 * splits / element bytes) == 0) and part s
+// writes its fp32 partial product to C + s * M * N.  The partials are summed
+// into the residual stream, in split order, by launch_resid_ln.
+void launch_gemm_splitk(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
+                        int N, int K, int splits, float* partials, hipStream_t s);
+
+// x += partials[0] + ... + partials[splits-1] (in that order), then the
+// bias-free LayerNorm (gamma non-null) or plain conversion (gamma null) of
+// the new x to out (fp32 / bf16 / 7-bit codes + scales), or no output
+// (out_kind < 0).  One wave per row.
+void launch_resid_ln(float* x, const float* partials, int splits, const float* gamma, int rows, int width, float eps,
+                     int out_kind, void* out, float* out_scale, hipStream_t s);
 
 // QKV projection with the RoPE / transposed-V epilogue: writes rotated Q
 // and K into qkv [M, 3H] (columns 0 .. 2H-1) and V into qo.vt.  Requires

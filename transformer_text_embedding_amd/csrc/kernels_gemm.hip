@@ -128,7 +128,7 @@ template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES>
 __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
                                               const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
                                               void* __restrict__ C, int M, int N, int K, int n_blocks,
-                                              int m_blocks, QkvOut qo) {
+                                              int m_blocks, int splits, QkvOut qo) {
   using F = Fmt<PREC>;
   using G = Cfg<WM, WN, PREC, STAGES>;
   constexpr int BM = G::BM, BN = G::BN;
@@ -144,7 +144,9 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
   // spans about half of A's rows and a quarter of W's, which together fit
   // that XCD's L2.
   const int n_tiles = n_blocks * m_blocks;
-  const int xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  // split-K: block b computes K part b / n_tiles of tile b % n_tiles
+  const int split = blockIdx.x / n_tiles, tile_bid = blockIdx.x - split * n_tiles;
+  const int xcd = tile_bid & 7, local = tile_bid >> 3;
   const int per = n_tiles >> 3, extra = n_tiles & 7;
   const int tile = xcd * per + min(xcd, extra) + local;
   const int grp = max(1, n_blocks >> 2);
@@ -153,7 +155,8 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
   const int mb = grem / gwidth, nb = gbase + grem % gwidth;
   const int m0 = mb * BM;
   const size_t row_bytes = (size_t)K * F::ES;
-  const int nk = K / F::BK;
+  const int k_part = K / splits;  // elements of K this block reduces over
+  const int nk = k_part / F::BK;
 
   // load plan: instruction j of this wave fills LDS rows 8q .. 8q+7 of the
   // tile (q = wid * QW + j); lane -> row 8q + lane/8, slot lane%8, which
@@ -164,14 +167,15 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
   for (int j = 0; j < G::QW; ++j) {
     const int r = 8 * (wid * G::QW + j) + (lane >> 3);
     if (r < BM)
-      src[j] = A + (size_t)min(m0 + r, M - 1) * row_bytes + chunk * 16;
+      src[j] = A + (size_t)min(m0 + r, M - 1) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
     else
-      src[j] = W + (size_t)w_row<EPI, BN>(r - BM, nb, N) * row_bytes + chunk * 16;
+      src[j] = W + (size_t)w_row<EPI, BN>(r - BM, nb, N) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
   }
   // int8: lanes 0..31 of wave w load the 4 block scales (16 bytes) of W row
   // 32 w + lane of the tile.
   const float* s_src = nullptr;
-  if constexpr (PREC == P_I8) s_src = w_scale + (size_t)w_row<EPI, BN>(wid * 32 + (lane & 31), nb, N) * (K / 32);
+  if constexpr (PREC == P_I8)
+    s_src = w_scale + (size_t)w_row<EPI, BN>(wid * 32 + (lane & 31), nb, N) * (K / 32) + split * (k_part / 32);
 
   f32x4 acc[WM][WN];
 #pragma unroll
@@ -346,6 +350,8 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
           const float v = acc[mt][nt][r] * rs;
           if constexpr (EPI == E_RESID) {
             reinterpret_cast<float*>(C)[(size_t)m * N + n] += v;
+          } else if constexpr (EPI == E_PART) {
+            reinterpret_cast<float*>(C)[((size_t)split * M + m) * N + n] = v;
           } else if constexpr (OUT == O_BF16) {
             reinterpret_cast<uint16_t*>(C)[(size_t)m * N + n] = f32_to_bf16(v);
           } else {
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
 
 template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES = 4>
 void go(const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N, int K, void* C,
-        hipStream_t s, const QkvOut& qo = QkvOut{}) {
+        hipStream_t s, const QkvOut& qo = QkvOut{}, int splits = 1) {
   using G = Cfg<WM, WN, PREC, STAGES>;
   static bool attr_set = false;  // once per instantiation
   if (!attr_set) {
@@ -369,9 +375,9 @@ void go(const void* A, const float* a_scale, const void* W, const float* w_scale
   }
   const int n_blocks = EPI == E_GEGLU ? N / (G::BN / 2) : N / G::BN;
   const int m_blocks = (M + G::BM - 1) / G::BM;
-  k_gemm<PREC, EPI, OUT, WM, WN, STAGES><<<n_blocks * m_blocks, 256, G::LDS, s>>>(reinterpret_cast<const uint8_t*>(A), a_scale,
+  k_gemm<PREC, EPI, OUT, WM, WN, STAGES><<<n_blocks * m_blocks * splits, 256, G::LDS, s>>>(reinterpret_cast<const uint8_t*>(A), a_scale,
                                                  reinterpret_cast<const uint8_t*>(W), w_scale, C, M, N, K, n_blocks,
-                                                 m_blocks, qo);
+                                                 m_blocks, splits, qo);
 }
 
 template <int PREC, int WM, int ST>
@@ -429,6 +435,23 @@ void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const v
   if (prec == P_F32) launch_prec<P_F32>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
   else if (prec == P_BF16) launch_prec<P_BF16>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
   else launch_prec<P_I8>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+}
+
+void launch_gemm_splitk(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
+                        int N, int K, int splits, float* partials, hipStream_t s) {
+  if (M <= 0) return;
+  // 64 x 128 tiles; a third stage when each part is long
+  const bool long_k = K / splits > 1024;
+  if (prec == P_F32) {
+    if (long_k) go<P_F32, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    else go<P_F32, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+  } else if (prec == P_BF16) {
+    if (long_k) go<P_BF16, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    else go<P_BF16, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+  } else {
+    if (long_k) go<P_I8, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    else go<P_I8, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+  }
 }
 
 void launch_gemm_qkv(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int K,

@@ -197,6 +197,44 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ x, const f
 }
 
 // --------------------------------------------------------------------------
+// residual update from split-K partial products, fused with the next norm
+// --------------------------------------------------------------------------
+
+// x[r] += p_0[r] + ... + p_{S-1}[r] (in split order), written back; then
+// LayerNorm / conversion / quantisation of the updated row into out
+// (WRITE = false: the residual update only).
+template <int EPL, int OUT, bool NORM, bool WRITE>
+__global__ __launch_bounds__(256) void k_resid_ln(float* __restrict__ x, const float* __restrict__ partials,
+                                                  int splits, const float* __restrict__ gamma, int rows, float eps,
+                                                  void* __restrict__ out, float* __restrict__ out_scale) {
+  using RS = RowShape<EPL>;
+  constexpr int Wd = RS::W;
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= rows) return;
+  float v[EPL];
+  load_f32_row<EPL>(x + (size_t)r * Wd, lane, v);
+  for (int sp = 0; sp < splits; ++sp) {
+    float p[EPL];
+    load_f32_row<EPL>(partials + ((size_t)sp * rows + r) * Wd, lane, p);
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] += p[i];
+  }
+  store_f32_row<EPL>(x + (size_t)r * Wd, lane, v);
+  if constexpr (WRITE) {
+    if constexpr (NORM) layernorm_regs<EPL>(v, gamma, lane, eps);
+    if constexpr (OUT == O_F32) {
+      store_f32_row<EPL>(reinterpret_cast<float*>(out) + (size_t)r * Wd, lane, v);
+    } else if constexpr (OUT == O_BF16) {
+      store_bf16_row<EPL>(reinterpret_cast<uint16_t*>(out) + (size_t)r * Wd, lane, v);
+    } else {
+      const float s = store_q7_row<EPL>(reinterpret_cast<int8_t*>(out) + (size_t)r * Wd, lane, v);
+      if (lane == 0) out_scale[r] = s;
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
 // final LayerNorm + mean pool + L2 normalisation
 // --------------------------------------------------------------------------
 
@@ -336,6 +374,32 @@ void launch_ln(const float* x, const float* gamma, int rows, int width, float ep
 
 void launch_quant7(const float* x, int rows, int width, int8_t* q, float* scale, hipStream_t s) {
   launch_ln(x, nullptr, rows, width, 0.f, O_I8, q, scale, s);
+}
+
+void launch_resid_ln(float* x, const float* partials, int splits, const float* gamma, int rows, int width, float eps,
+                     int out_kind, void* out, float* out_scale, hipStream_t s) {
+  if (rows <= 0) return;
+  const dim3 grid((rows + 3) / 4), block(256);
+#define L_RLN(E)                                                                                                      \
+  if (out_kind < 0) {                                                                                                 \
+    k_resid_ln<E, O_F32, false, false><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);  \
+  } else if (gamma) {                                                                                                 \
+    if (out_kind == O_F32)                                                                                            \
+      k_resid_ln<E, O_F32, true, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);  \
+    else if (out_kind == O_BF16)                                                                                      \
+      k_resid_ln<E, O_BF16, true, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale); \
+    else                                                                                                              \
+      k_resid_ln<E, O_I8, true, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);   \
+  } else {                                                                                                            \
+    if (out_kind == O_F32)                                                                                            \
+      k_resid_ln<E, O_F32, false, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale); \
+    else if (out_kind == O_BF16)                                                                                      \
+      k_resid_ln<E, O_BF16, false, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);\
+    else                                                                                                              \
+      k_resid_ln<E, O_I8, false, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);  \
+  }
+  TTE_EPL_DISPATCH(width, L_RLN)
+#undef L_RLN
 }
 
 void launch_pool(const float* x, const float* gamma, float eps, int H, const int* d_off, const int* d_unit,

@@ -33,7 +33,7 @@ tte_status fail(tte_status s, const std::string& msg) {
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t x, xa, ascale, qkv, vt, o, y, seg, off, unit, partial, cosg, sing, cosl, sinl, total;
+  size_t x, xa, ascale, qkv, vt, o, y, kpart, seg, off, unit, partial, cosg, sing, cosl, sinl, total;
   int max_units;
   int vt_stride;
 };
@@ -61,6 +61,7 @@ Layout layout_of(const tte_config& c) {
   L.vt = take(H * (size_t)L.vt_stride * ab);
   L.o = take(T * H * ab);
   L.y = take(T * I * ab);
+  L.kpart = take(c.flags & TTE_FLAG_SPLIT_K ? 2 * T * H * 4 : 0);  // split-K partials of the down-projection
   L.seg = take(T * sizeof(Seg));
   L.off = take(((size_t)c.max_texts + 1) * 4);
   L.unit = take(((size_t)c.max_texts + 1) * 4);
@@ -95,6 +96,7 @@ bool check_config(const tte_config* c, std::string* why) {
   if (c->max_tokens <= 0 || c->max_text_len <= 0 || c->max_texts <= 0)
     return bad("max_tokens, max_text_len and max_texts must be positive");
   if (c->max_tokens > (1 << 24)) return bad("max_tokens above 2^24");
+  if (c->flags & ~int32_t(TTE_FLAG_SPLIT_K)) return bad("unknown flag");
   return true;
 }
 
@@ -134,6 +136,7 @@ struct tte_model {
   void* vt;
   void* o;
   void* y;
+  float* kpart;
   Seg* seg;
   int* d_off;
   int* d_unit;
@@ -256,6 +259,14 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
   }
   if (d_states) (void)hipMemcpyAsync(d_states, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
 
+  // With TTE_FLAG_SPLIT_K the down-projection of a short pack runs split-K
+  // (its H-wide output gives fewer 64 x 128 tiles than there are compute
+  // units); its two partial products are added to the residual stream by the
+  // next norm kernel.
+  const int o2_splits =
+      ((c.flags & TTE_FLAG_SPLIT_K) && I >= 2048 && ((T + 63) / 64) * (H / 128) < 256) ? 2 : 1;
+  bool pending = false;  // x still lacks the partials of the last down-projection
+  const int in_fmt = P == TTE_INT8 ? O_I8 : act;
   for (int l = 0; l < n_run; ++l) {
     const tte_layer_weights& LW = m->layers[l];
     const int glob = (l % c.global_every) == 0;
@@ -263,9 +274,13 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
     const void* a_in = m->xa;
     if (P == TTE_FP32 && l == 0) {
       a_in = m->x;
+    } else if (pending) {
+      ProfScope ps(m, TTE_K_NORM, s);
+      launch_resid_ln(m->x, m->kpart, o2_splits, LW.attn_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
+      pending = false;
     } else {
       ProfScope ps(m, P == TTE_INT8 && l == 0 ? TTE_K_QUANT : TTE_K_NORM, s);
-      launch_ln(m->x, l == 0 ? nullptr : LW.attn_norm, T, H, c.ln_eps, P == TTE_INT8 ? O_I8 : act, m->xa, m->ascale, s);
+      launch_ln(m->x, l == 0 ? nullptr : LW.attn_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
     }
     {
       ProfScope ps(m, TTE_K_GEMM_QKV, s);
@@ -289,7 +304,7 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
     }
     {
       ProfScope ps(m, TTE_K_NORM, s);
-      launch_ln(m->x, LW.mlp_norm, T, H, c.ln_eps, P == TTE_INT8 ? O_I8 : act, m->xa, m->ascale, s);
+      launch_ln(m->x, LW.mlp_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
     }
     {
       ProfScope ps(m, TTE_K_GEMM_GEGLU, s);
@@ -303,7 +318,18 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
     }
     {
       ProfScope ps(m, TTE_K_GEMM_O2, s);
-      launch_gemm(P, E_RESID, y_in, m->ascale, LW.wo2, LW.wo2_scale, T, H, I, m->x, O_F32, s);
+      if (o2_splits > 1) {
+        launch_gemm_splitk(P, y_in, m->ascale, LW.wo2, LW.wo2_scale, T, H, I, o2_splits, m->kpart, s);
+        pending = true;
+      } else {
+        launch_gemm(P, E_RESID, y_in, m->ascale, LW.wo2, LW.wo2_scale, T, H, I, m->x, O_F32, s);
+      }
+    }
+    if (pending && (d_states || l + 1 == n_run)) {
+      // a trace copies x, and pooling reads it: apply the partials now
+      ProfScope ps(m, TTE_K_NORM, s);
+      launch_resid_ln(m->x, m->kpart, o2_splits, nullptr, T, H, c.ln_eps, -1, nullptr, nullptr, s);
+      pending = false;
     }
     if (d_states) (void)hipMemcpyAsync(d_states + (size_t)(l + 1) * T * H, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
   }
@@ -378,6 +404,7 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   m->vt = b + L.vt;
   m->o = b + L.o;
   m->y = b + L.y;
+  m->kpart = reinterpret_cast<float*>(b + L.kpart);
   m->seg = reinterpret_cast<Seg*>(b + L.seg);
   m->d_off = reinterpret_cast<int*>(b + L.off);
   m->d_unit = reinterpret_cast<int*>(b + L.unit);
@@ -487,6 +514,38 @@ tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, con
   (void)hipGetLastError();
   launch_gemm(precision, epilogue, d_a, d_a_scale, d_w, d_w_scale, M, N, K, d_c, out_kind,
               reinterpret_cast<hipStream_t>(stream));
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+tte_status tte_op_gemm_splitk(int32_t precision, const void* d_a, const float* d_a_scale, const void* d_w,
+                              const float* d_w_scale, int32_t M, int32_t N, int32_t K, int32_t splits,
+                              float* d_partials, void* stream) {
+  if (precision < TTE_FP32 || precision > TTE_INT8) return fail(TTE_E_INVALID, "bad precision");
+  if (M < 0 || N <= 0 || K <= 0 || splits < 1) return fail(TTE_E_INVALID, "M must be >= 0, N, K, splits > 0");
+  const int es = precision == TTE_FP32 ? 4 : (precision == TTE_BF16 ? 2 : 1);
+  if (N % 128 != 0 || K % splits != 0 || ((K / splits) * es) % 128 != 0)
+    return fail(TTE_E_UNSUPPORTED, "N must be a multiple of 128 and each K part a multiple of 128 bytes");
+  if (M == 0) return TTE_OK;
+  if (!d_a || !d_w || !d_partials || (precision == TTE_INT8 && (!d_a_scale || !d_w_scale)))
+    return fail(TTE_E_INVALID, "NULL buffer");
+  (void)hipGetLastError();
+  launch_gemm_splitk(precision, d_a, d_a_scale, d_w, d_w_scale, M, N, K, splits, d_partials,
+                     reinterpret_cast<hipStream_t>(stream));
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+tte_status tte_op_resid_ln(float* d_x, const float* d_partials, int32_t splits, const float* d_gamma, int32_t rows,
+                           int32_t width, float eps, int32_t out_kind, void* d_out, float* d_scale, void* stream) {
+  if (rows < 0 || splits < 0) return fail(TTE_E_INVALID, "rows and splits must be >= 0");
+  if (!row_width_supported(width)) return fail(TTE_E_UNSUPPORTED, "unsupported row width");
+  if (out_kind < -1 || out_kind > TTE_OUT_I8) return fail(TTE_E_INVALID, "bad out_kind");
+  if (rows == 0) return TTE_OK;
+  if (!d_x || (splits > 0 && !d_partials) || (out_kind >= 0 && !d_out) || (out_kind == TTE_OUT_I8 && !d_scale))
+    return fail(TTE_E_INVALID, "NULL buffer");
+  if (d_gamma && !(eps > 0.f)) return fail(TTE_E_INVALID, "eps must be > 0");
+  (void)hipGetLastError();
+  launch_resid_ln(d_x, d_partials, splits, d_gamma, rows, width, eps, out_kind, d_out, d_scale,
+                  reinterpret_cast<hipStream_t>(stream));
   return hip_check(hipGetLastError(), "kernel launch");
 }
 
