@@ -77,10 +77,13 @@ def test_layernorm_to_int8_codes():
 # GEMMs
 # --------------------------------------------------------------------------
 
-# tile configurations: 32x128 (few narrow tiles), 64x128, 64x128 with 3
-# stages (K > 1024), 128x128 (>= 1024 tiles of 128x128)
-SHAPES = [(178, 384, 128), (957, 2304, 768), (300, 768, 3072), (130, 512, 256), (1, 128, 128), (4100, 4096, 128)]
-GEGLU_SHAPES = [(178, 256, 128), (957, 3072, 768), (65, 64, 256), (2100, 4096, 128)]
+# tile configurations: 4-wave 32x128 (few narrow tiles), 64x128, 64x128 with
+# 3 stages (K > 1024), 128x128 (int8, >= 1024 tiles); 8-wave 128x128 (wide
+# fp32 / bf16 products) and 256x256 (>= 512 such tiles, or residual
+# products of >= 8k rows)
+SHAPES = [(178, 384, 128), (957, 2304, 768), (300, 768, 3072), (130, 512, 256), (1, 128, 128), (4100, 4096, 128),
+          (8200, 768, 3072)]
+GEGLU_SHAPES = [(178, 256, 128), (957, 3072, 768), (65, 64, 256), (2100, 4096, 128), (8192, 3072, 768)]
 
 
 def _run_gemm(prec, epi, a, a_s, w, w_s, M, N, K, c, out_kind):

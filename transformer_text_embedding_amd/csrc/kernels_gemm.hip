@@ -47,41 +47,47 @@ namespace tte {
 
 namespace {
 
-constexpr int KT_BYTES = 128;      // bytes of K per tile row
-constexpr int ROW = 128;           // LDS row (bytes)
-constexpr int SCALE_BYTES = 2048;  // int8: fp32 scales of 4 blocks x 128 W rows
 
 template <int PREC>
 struct Fmt {
   static constexpr int ES = PREC == P_F32 ? 4 : (PREC == P_BF16 ? 2 : 1);
-  static constexpr int BK = KT_BYTES / ES;
 };
 
-template <int WM, int WN, int PREC, int STAGES_ = 4>
+// Block of WGM x WGN waves; each wave owns WM x WN MFMA 16x16 output tiles.
+// A K tile is KT bytes of every operand row (128: 32 fp32, 64 bf16 or 128
+// int8; 64: half that, fp32 and bf16 only), one LDS row each.
+template <int WM, int WN, int PREC, int STAGES_, int WGM, int WGN, int KT_ = 128>
 struct Cfg {
-  static constexpr int BM = 32 * WM;
-  static constexpr int BN = 32 * WN;
+  static constexpr int KT = KT_;
+  static constexpr int BK = KT / Fmt<PREC>::ES;  // K elements per tile
+  static constexpr int NW = WGM * WGN;  // waves per block
+  static constexpr int THREADS = 64 * NW;
+  static constexpr int BM = 16 * WM * WGM;
+  static constexpr int BN = 16 * WN * WGN;
   static constexpr int ROWS = BM + BN;
-  static constexpr int TILE = ROWS * ROW + (PREC == P_I8 ? SCALE_BYTES : 0);
+  static constexpr int SCALE_BYTES = PREC == P_I8 ? BN * 16 : 0;  // int8: fp32 scales of 4 blocks per W row
+  static constexpr int TILE = ROWS * KT + SCALE_BYTES;
   static constexpr int STAGES = STAGES_;
   static constexpr int LDS = STAGES * TILE;
-  static constexpr int Q = ROWS / 8;  // 1 KB load instructions per K tile
-  static constexpr int QW = Q / 4;    // per wave
+  static constexpr int Q = ROWS * KT / 1024;  // 1 KB load instructions per K tile
+  static constexpr int QW = Q / NW;           // per wave
   static constexpr int PER_TILE = QW + (PREC == P_I8 ? 1 : 0);  // vector-memory ops per wave per tile
-  static_assert(Q % 4 == 0, "tile rows must split evenly over 4 waves");
-  static_assert(PREC != P_I8 || BN == 128, "int8 scale staging assumes 128 W rows");
+  static_assert(ROWS * KT % 1024 == 0 && Q % NW == 0, "tile rows must split evenly over the waves");
+  static_assert(QW * NW * 1024 == ROWS * KT, "the load instructions cover the tile exactly");
+  static_assert(PREC != P_I8 || BN == 32 * NW, "int8 scale staging: 32 W rows per wave");
+  static_assert(KT == 128 || (KT == 64 && PREC != P_I8), "K tile of 128 bytes, or 64 for fp32 / bf16");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
-// Row of W that tile row r of n-block nb reads.  GEGLU: in each wave's half
-// of the tile (BN/2 rows), the first BN/4 rows are GELU-half rows n and the
-// last BN/4 the matching gate rows N + n.
-template <int EPI, int BN>
+// Row of W that tile row r of n-block nb reads.  GEGLU: in each wave
+// column's share of the tile (BN/WGN rows), the first half are GELU-half
+// rows n and the second half the matching gate rows N + n.
+template <int EPI, int BN, int WGN>
 __device__ __forceinline__ int w_row(int r, int nb, int N) {
   if constexpr (EPI == E_GEGLU) {
-    constexpr int HW = BN / 2, QW_ = BN / 4;
-    const int half_wave = r / HW, within = r % HW;
-    const int base = nb * (BN / 2) + half_wave * QW_;
+    constexpr int HW = BN / WGN, QW_ = HW / 2;
+    const int wave_col = r / HW, within = r % HW;
+    const int base = nb * (BN / 2) + wave_col * QW_;
     return within < QW_ ? base + within : N + base + (within - QW_);
   } else {
     return nb * BN + r;
@@ -113,29 +119,30 @@ __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
 
 // Issue the direct-to-LDS loads of K tile kt into `stage`: QW 1 KB
 // instructions of A/W rows, and for int8 the 16-byte scale vectors of 32 W
-// rows (lanes 0..31).
-template <int QW, int PREC>
+// rows (lanes 0..31 of every wave).
+template <int QW, int PREC, int KT>
 __device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* const* src, const float* s_src, int kt,
                                            int wid, int lane, int rows) {
 #pragma unroll
-  for (int j = 0; j < QW; ++j) dma16(src[j] + (size_t)kt * KT_BYTES, stage + (wid * QW + j) * 1024);
+  for (int j = 0; j < QW; ++j) dma16(src[j] + (size_t)kt * KT, stage + (wid * QW + j) * 1024);
   if constexpr (PREC == P_I8) {
-    if (lane < 32) dma16(s_src + kt * 4, stage + rows * ROW + wid * 512);
+    if (lane < 32) dma16(s_src + kt * 4, stage + rows * KT + wid * 512);
   }
 }
 
-template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES>
-__global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
+template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES, int WGM, int WGN, int KT>
+__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
                                               const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
                                               void* __restrict__ C, int M, int N, int K, int n_blocks,
                                               int m_blocks, int splits, QkvOut qo) {
   using F = Fmt<PREC>;
-  using G = Cfg<WM, WN, PREC, STAGES>;
+  using G = Cfg<WM, WN, PREC, STAGES, WGM, WGN, KT>;
   constexpr int BM = G::BM, BN = G::BN;
+  constexpr int ROW = KT;  // LDS row bytes
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  const int wm = wid >> 1, wn = wid & 1;
+  const int wm = wid / WGN, wn = wid % WGN;
   const int g = lane >> 4, li = lane & 15;
 
   // XCD-aware tile order: block b runs on XCD b mod 8; XCD x gets a
@@ -156,26 +163,35 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
   const int m0 = mb * BM;
   const size_t row_bytes = (size_t)K * F::ES;
   const int k_part = K / splits;  // elements of K this block reduces over
-  const int nk = k_part / F::BK;
+  const int nk = k_part / G::BK;
 
-  // load plan: instruction j of this wave fills LDS rows 8q .. 8q+7 of the
-  // tile (q = wid * QW + j); lane -> row 8q + lane/8, slot lane%8, which
-  // holds chunk slot ^ (row & 7) = (lane & 7) ^ (lane >> 3).
-  const int chunk = (lane & 7) ^ (lane >> 3);
+  // LDS rows are unpadded and the 16-byte chunk c of row r sits in slot
+  // c ^ swizzle(r), so that the rows a fragment read touches (16
+  // consecutive rows, one chunk) spread over distinct bank groups:
+  //   KT = 128 (8 chunks): swizzle(r) = r & 7;
+  //   KT = 64 (4 chunks):  swizzle(r) = ((r >> 1) ^ (r >> 3)) & 3, which
+  //   puts any 8 consecutive rows in 8 distinct slots of a 128-byte window
+  //   and 16 consecutive rows in 16 distinct slots of 256 bytes.
+  // Load plan: instruction j of this wave fills the 1 KB of LDS rows
+  // RPI q .. RPI q + RPI - 1 (q = wid * QW + j); lane -> row RPI q + lane /
+  // (KT/16), slot lane % (KT/16), which holds chunk slot ^ swizzle(row).
+  constexpr int CPRW = KT / 16, RPI = 1024 / KT;  // chunks per row, rows per load instruction
+  const int lrow = lane / CPRW;  // row within the instruction's rows (= row mod RPI)
+  const int chunk = KT == 128 ? ((lane & 7) ^ lrow) : ((lane & 3) ^ (((lrow >> 1) ^ (lrow >> 3)) & 3));
   const uint8_t* src[G::QW];
 #pragma unroll
   for (int j = 0; j < G::QW; ++j) {
-    const int r = 8 * (wid * G::QW + j) + (lane >> 3);
+    const int r = RPI * (wid * G::QW + j) + lrow;
     if (r < BM)
       src[j] = A + (size_t)min(m0 + r, M - 1) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
     else
-      src[j] = W + (size_t)w_row<EPI, BN>(r - BM, nb, N) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
+      src[j] = W + (size_t)w_row<EPI, BN, WGN>(r - BM, nb, N) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
   }
   // int8: lanes 0..31 of wave w load the 4 block scales (16 bytes) of W row
   // 32 w + lane of the tile.
   const float* s_src = nullptr;
   if constexpr (PREC == P_I8)
-    s_src = w_scale + (size_t)w_row<EPI, BN>(wid * 32 + (lane & 31), nb, N) * (K / 32) + split * (k_part / 32);
+    s_src = w_scale + (size_t)w_row<EPI, BN, WGN>(wid * 32 + (lane & 31), nb, N) * (K / 32) + split * (k_part / 32);
 
   f32x4 acc[WM][WN];
 #pragma unroll
@@ -184,9 +200,9 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
     for (int b = 0; b < WN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int p = 0; p < G::STAGES - 1 && p < nk; ++p)
-    issue_tile<G::QW, PREC>(smem + p * G::TILE, src, s_src, p, wid, lane, G::ROWS);
+    issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, src, s_src, p, wid, lane, G::ROWS);
 
-  const int swz = li & 7;
+  const int swz = KT == 128 ? (li & 7) : (((li >> 1) ^ (li >> 3)) & 3);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of tile kt are done once at most `ahead` tiles of
     // its own loads remain in flight; the barrier publishes every wave's
@@ -195,7 +211,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
     __builtin_amdgcn_s_barrier();
     // the stage of tile kt - 1 is free: every wave finished reading it
     if (kt + G::STAGES - 1 < nk)
-      issue_tile<G::QW, PREC>(smem + ((kt + G::STAGES - 1) % G::STAGES) * G::TILE, src, s_src, kt + G::STAGES - 1,
+      issue_tile<G::QW, PREC, KT>(smem + ((kt + G::STAGES - 1) % G::STAGES) * G::TILE, src, s_src, kt + G::STAGES - 1,
                               wid, lane, G::ROWS);
 
     const uint8_t* stage = smem + (kt % G::STAGES) * G::TILE;
@@ -204,7 +220,7 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
 
     if constexpr (PREC == P_F32 || PREC == P_BF16) {
 #pragma unroll
-      for (int cc = 0; cc < 2; ++cc) {
+      for (int cc = 0; cc < KT / 64; ++cc) {
         const int off = ((4 * cc + g) ^ swz) << 4;
         if constexpr (PREC == P_F32) {
           f32x4 af[WM], bf[WN];
@@ -327,83 +343,128 @@ __global__ __launch_bounds__(256) void k_gemm(const uint8_t* __restrict__ A, con
     }
     return;
   }
+  // Other epilogues: the wave's results pass through LDS one 16-row slab at
+  // a time (row-major, rows padded by 16 bytes so that the 4 row groups of
+  // a write land in different banks) and leave as 16-byte vectors of whole
+  // rows; the residual form reads, adds and writes 16 bytes at a time.
+  constexpr bool F32_OUT = EPI == E_RESID || EPI == E_PART || OUT == O_F32;
+  constexpr int OES = F32_OUT ? 4 : 2;                     // output element bytes
+  constexpr int NT_OUT = EPI == E_GEGLU ? WN / 2 : WN;     // 16-column output tiles per wave
+  constexpr int CW = 16 * NT_OUT;                          // output columns per wave
+  constexpr int RB = CW * OES + 16;                        // LDS bytes per staged row
+  constexpr int CPR = CW * OES / 16;                       // 16-byte chunks per row
+  static_assert(G::NW * 16 * RB <= G::LDS, "staging fits the K-tile ring");
+  __syncthreads();  // every wave is done with the K-tile ring
+  uint8_t* slab = smem + wid * 16 * RB;
+  const int n_wave = EPI == E_GEGLU ? nb * (BN / 2) + wn * CW : nb * BN + wn * CW;
 #pragma unroll
   for (int mt = 0; mt < WM; ++mt) {
+    const int m_slab = m0 + wm * 16 * WM + mt * 16;
+    float rs[4] = {1.f, 1.f, 1.f, 1.f};
+    if constexpr (PREC == P_I8) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int m = m0 + wm * 16 * WM + mt * 16 + 4 * g + r;
-      if (m >= M) continue;
-      float rs = 1.f;
-      if constexpr (PREC == P_I8) rs = a_scale[m];
-      if constexpr (EPI == E_GEGLU) {
+      for (int r = 0; r < 4; ++r) rs[r] = a_scale[min(m_slab + 4 * g + r, M - 1)];
+    }
 #pragma unroll
-        for (int nt = 0; nt < WN / 2; ++nt) {
-          const int n = nb * (BN / 2) + wn * (BN / 4) + nt * 16 + li;
-          const float v = gelu_erf(acc[mt][nt][r] * rs) * (acc[mt][nt + WN / 2][r] * rs);
-          if constexpr (OUT == O_BF16) reinterpret_cast<uint16_t*>(C)[(size_t)m * N + n] = f32_to_bf16(v);
-          else reinterpret_cast<float*>(C)[(size_t)m * N + n] = v;
-        }
+    for (int nt = 0; nt < NT_OUT; ++nt) {
+      float v[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if constexpr (EPI == E_GEGLU) v[r] = gelu_erf(acc[mt][nt][r] * rs[r]) * (acc[mt][nt + WN / 2][r] * rs[r]);
+        else v[r] = acc[mt][nt][r] * rs[r];
+      }
+      uint8_t* p = slab + (4 * g) * RB + (nt * 16 + li) * OES;
+      if constexpr (F32_OUT) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) *reinterpret_cast<float*>(p + r * RB) = v[r];
       } else {
-#pragma unroll
-        for (int nt = 0; nt < WN; ++nt) {
-          const int n = nb * BN + wn * 16 * WN + nt * 16 + li;
-          const float v = acc[mt][nt][r] * rs;
-          if constexpr (EPI == E_RESID) {
-            reinterpret_cast<float*>(C)[(size_t)m * N + n] += v;
-          } else if constexpr (EPI == E_PART) {
-            reinterpret_cast<float*>(C)[((size_t)split * M + m) * N + n] = v;
-          } else if constexpr (OUT == O_BF16) {
-            reinterpret_cast<uint16_t*>(C)[(size_t)m * N + n] = f32_to_bf16(v);
-          } else {
-            reinterpret_cast<float*>(C)[(size_t)m * N + n] = v;
-          }
-        }
+        const uint32_t lo = pack_bf16x2(v[0], v[1]), hi = pack_bf16x2(v[2], v[3]);
+        *reinterpret_cast<uint16_t*>(p) = (uint16_t)lo;
+        *reinterpret_cast<uint16_t*>(p + RB) = (uint16_t)(lo >> 16);
+        *reinterpret_cast<uint16_t*>(p + 2 * RB) = (uint16_t)hi;
+        *reinterpret_cast<uint16_t*>(p + 3 * RB) = (uint16_t)(hi >> 16);
       }
     }
+    // LDS operations of one wave complete in order: the reads below see the
+    // writes above, and the next slab's writes follow these reads
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int c = lane; c < 16 * CPR; c += 64) {
+      const int row = c / CPR, cc = c % CPR;
+      const int m = m_slab + row;
+      if (m >= M) continue;
+      const u32x4 d = *reinterpret_cast<const u32x4*>(slab + row * RB + cc * 16);
+      const int n = n_wave + cc * (16 / OES);
+      if constexpr (EPI == E_RESID) {
+        f32x4* cp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + (size_t)m * N + n);
+        f32x4 o = *cp;
+        o += __builtin_bit_cast(f32x4, d);
+        *cp = o;
+      } else if constexpr (EPI == E_PART) {
+        *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(C) + ((size_t)split * M + m) * N + n) = d;
+      } else {
+        *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(C) + ((size_t)m * N + n) * OES) = d;
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
   }
 }
 
-template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES = 4>
+template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES = 4, int WGM = 2, int WGN = 2, int KT = 128>
 void go(const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N, int K, void* C,
         hipStream_t s, const QkvOut& qo = QkvOut{}, int splits = 1) {
-  using G = Cfg<WM, WN, PREC, STAGES>;
+  using G = Cfg<WM, WN, PREC, STAGES, WGM, WGN, KT>;
   static bool attr_set = false;  // once per instantiation
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<PREC, EPI, OUT, WM, WN, STAGES>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<PREC, EPI, OUT, WM, WN, STAGES, WGM, WGN, KT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
     attr_set = true;
   }
   const int n_blocks = EPI == E_GEGLU ? N / (G::BN / 2) : N / G::BN;
   const int m_blocks = (M + G::BM - 1) / G::BM;
-  k_gemm<PREC, EPI, OUT, WM, WN, STAGES><<<n_blocks * m_blocks * splits, 256, G::LDS, s>>>(reinterpret_cast<const uint8_t*>(A), a_scale,
+  k_gemm<PREC, EPI, OUT, WM, WN, STAGES, WGM, WGN, KT><<<n_blocks * m_blocks * splits, G::THREADS, G::LDS, s>>>(reinterpret_cast<const uint8_t*>(A), a_scale,
                                                  reinterpret_cast<const uint8_t*>(W), w_scale, C, M, N, K, n_blocks,
                                                  m_blocks, splits, qo);
 }
 
-template <int PREC, int WM, int ST>
+template <int PREC, int WM, int ST, int WGM = 2, int WGN = 2>
 void go_prec(int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N, int K,
              void* C, int out_kind, hipStream_t s) {
   if (epi == E_RESID) {
-    go<PREC, E_RESID, O_F32, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
+    go<PREC, E_RESID, O_F32, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
   } else if (epi == E_GEGLU) {
-    if (out_kind == O_BF16) go<PREC, E_GEGLU, O_BF16, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
-    else go<PREC, E_GEGLU, O_F32, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
+    if (out_kind == O_BF16) go<PREC, E_GEGLU, O_BF16, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
+    else go<PREC, E_GEGLU, O_F32, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
   } else {
-    if (out_kind == O_BF16) go<PREC, E_STORE, O_BF16, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
-    else go<PREC, E_STORE, O_F32, WM, 4, ST>(A, a_scale, W, w_scale, M, N, K, C, s);
+    if (out_kind == O_BF16) go<PREC, E_STORE, O_BF16, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
+    else go<PREC, E_STORE, O_F32, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
   }
 }
 
 // Tile choice, measured on MI355X (bf16, the encoder's shapes at 1.9k and
-// 16k tokens): 128 x 128 once there are >= 1024 such tiles; else 32 x 128
-// for narrow, short-K products with few tiles (the 768-wide attention
-// output of a ~2k-token pack); else
-// 64 x 128, with a third stage for long K.
-enum TileCfg { T32, T64, T64L, T128 };
+// 16k tokens; 2 LDS stages of 128-byte K tiles unless noted):
+//  * T256: 256 x 256, 8 waves of 128 x 64 (one block per CU): wide products
+//    with >= 512 such tiles, and the residual products of >= 8k rows;
+//  * T128W8: 128 x 128, 8 waves of 32 x 64 (two blocks per CU): the other
+//    wide products (QKV always, GeGLU below the T256 size);
+//  * the 4-wave tiles for the 768-wide residual products: 32 x 128 when
+//    there are few tiles and K is short, else 64 x 128 (a third stage for
+//    long K);
+//  * int8 keeps 4-wave tiles (its scale staging feeds 32 W rows per wave):
+//    128 x 128 once there are >= 1024 such tiles.
+enum TileCfg { T32, T64, T64L, T128, T128W8, T256 };
 
-TileCfg pick_tiles(int M, int n_cols, int K) {
+TileCfg pick_tiles(int prec, int epi, int M, int n_cols, int K) {
   const long tiles128 = (long)((M + 127) / 128) * (n_cols / 128);
-  if (tiles128 >= 1024) return T128;
+  const long tiles256 = (long)((M + 255) / 256) * (n_cols / 256);
+  if (prec == P_I8) {
+    if (tiles128 >= 1024) return T128;
+  } else if (epi == E_RESID) {
+    if (M >= 8192 && n_cols % 256 == 0) return T256;
+  } else {
+    if (tiles256 >= 512 && n_cols % 256 == 0) return T256;
+    return T128W8;
+  }
   if (tiles128 < 256 && n_cols <= 1024 && K <= 1024) return T32;
   return K > 1024 ? T64L : T64;
 }
@@ -411,10 +472,16 @@ TileCfg pick_tiles(int M, int n_cols, int K) {
 template <int PREC>
 void launch_prec(int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N,
                  int K, void* C, int out_kind, hipStream_t s) {
-  switch (pick_tiles(M, epi == E_GEGLU ? 2 * N : N, K)) {
+  switch (pick_tiles(PREC, epi, M, epi == E_GEGLU ? 2 * N : N, K)) {
     case T128: go_prec<PREC, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
     case T32: go_prec<PREC, 1, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
     case T64L: go_prec<PREC, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
+    case T128W8:
+      if constexpr (PREC != P_I8) go_prec<PREC, 2, 2, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+      break;
+    case T256:
+      if constexpr (PREC != P_I8) go_prec<PREC, 8, 2, 2, 4>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+      break;
     default: go_prec<PREC, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
   }
 }
@@ -423,8 +490,12 @@ template <int PREC, int OUT>
 void launch_qkv_prec(const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int K,
                      void* qkv, const QkvOut& qo, hipStream_t s) {
   const int N = 3 * qo.hidden;
-  if (pick_tiles(M, N, K) == T128) go<PREC, E_QKV, OUT, 4, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
-  else go<PREC, E_QKV, OUT, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+  if constexpr (PREC == P_I8) {
+    if (pick_tiles(PREC, E_QKV, M, N, K) == T128) go<PREC, E_QKV, OUT, 4, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+    else go<PREC, E_QKV, OUT, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+  } else {
+    go<PREC, E_QKV, OUT, 2, 4, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+  }
 }
 
 }  // namespace
