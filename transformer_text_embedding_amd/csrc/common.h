@@ -75,4 +75,27 @@ __device__ __forceinline__ float gelu_erf(float a) {
   return __builtin_fmaf(fabsf(a), h, 0.5f * a);
 }
 
+// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maxima (gfx9
+// encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14).
+__device__ __forceinline__ void wait_vm(int n) {
+  switch (n) {
+#define TTE_W(k) \
+  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | ((k) & 15) | ((((k) >> 4) & 3) << 14)); break;
+    TTE_W(0) TTE_W(1) TTE_W(2) TTE_W(3) TTE_W(4) TTE_W(5) TTE_W(6) TTE_W(7) TTE_W(8) TTE_W(9) TTE_W(10)
+    TTE_W(11) TTE_W(12) TTE_W(13) TTE_W(14) TTE_W(15) TTE_W(16) TTE_W(17) TTE_W(18) TTE_W(19) TTE_W(20)
+#undef TTE_W
+    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+  }
+}
+
+typedef __attribute__((address_space(3))) void* lds_ptr;
+
+// One direct-to-LDS load (global_load_lds_dwordx4): each lane's 16 bytes at
+// g go to LDS l + 16 * lane (l must be the same for the whole wave).  Kept
+// a plain (non-template) function: the builtin inside templated kernels
+// loses the host-side kernel stub in this compiler.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
+  __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
+}
+
 }  // namespace tte

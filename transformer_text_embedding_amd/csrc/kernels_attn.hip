@@ -41,29 +41,24 @@ constexpr int AQ = 64;   // queries per block
 constexpr int AKT = 64;  // keys per tile
 constexpr float NEG_INF = -__builtin_huge_valf();
 
-template <int PREC>
+template <int PREC, int STAGES_ = 2>
 struct AttnCfg {
   static constexpr int ES = PREC == P_F32 ? 4 : 2;
   static constexpr int ROWB = 64 * ES;                // bytes of a K row (64 dims) and a V^T row (64 keys)
   static constexpr int TILE = 2 * 64 * ROWB;          // K tile + V^T tile
-  static constexpr int LDS = 2 * TILE;                // double buffer
+  static constexpr int STAGES = STAGES_;              // ring of key tiles, STAGES - 1 in flight
+  static constexpr int LDS = STAGES * TILE;
   static constexpr int ROWS_PER_Q = 1024 / ROWB;      // rows per 1 KB load instruction
   static constexpr int QW = (2 * 64 / ROWS_PER_Q) / 4;  // load instructions per wave per tile
   static constexpr int ALIGN = 16 / ES;               // key alignment of a V^T row segment
 };
 
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
-}
-
-template <int PREC>
+template <int PREC, int STAGES>
 __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const void* __restrict__ vt, int vt_stride,
                                               void* __restrict__ out, const Seg* __restrict__ seg, int T, int nh,
                                               int is_global, int window, float scale_log2) {
-  using C = AttnCfg<PREC>;
-  __shared__ __attribute__((aligned(1024))) uint8_t smem[C::LDS];
+  using C = AttnCfg<PREC, STAGES>;
+  extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int H = nh * 64, ld = 3 * H;
   const int h = blockIdx.y;
   const int i0 = blockIdx.x * AQ;
@@ -90,7 +85,14 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
   const bool qvalid = qi < T;
   const int qrow = qvalid ? qi : T - 1;
   const Seg qs = seg[qrow];
-  const int q_start = qvalid ? qs.start : 0, q_end = qvalid ? qs.end : 0;
+  // keys this lane's query may see: [k_lo, k_lo + k_span) (its text, and on
+  // a local layer the window); an invalid query sees none
+  int k_lo = qs.start, k_hi = qs.end;
+  if (!is_global) {
+    k_lo = max(k_lo, qi - window);
+    k_hi = min(k_hi, qi + window + 1);
+  }
+  const unsigned k_span = qvalid ? (unsigned)(k_hi - k_lo) : 0u;
 
   // ---- Q fragment (already rotated) ----
   f32x4 qf[4];   // fp32: dims 16 kc + 4 g + e
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
   const int j_first = kstart & ~(C::ALIGN - 1);
   const int n_tiles = (kend - j_first + AKT - 1) / AKT;
   auto issue = [&](int t) {
-    uint8_t* stage = smem + (t & 1) * C::TILE;
+    uint8_t* stage = smem + (t % C::STAGES) * C::TILE;
     const int j0 = j_first + t * AKT;
 #pragma unroll
     for (int j = 0; j < C::QW; ++j) {
@@ -135,14 +137,17 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = NEG_INF, l_run = 0.f;
 
-  if (n_tiles > 0) issue(0);
+  for (int t = 0; t < C::STAGES - 1 && t < n_tiles; ++t) issue(t);
   for (int t = 0; t < n_tiles; ++t) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile t (and Q) are done
-    __builtin_amdgcn_s_barrier();        // every wave's are; tile t - 1's buffer is free
-    if (t + 1 < n_tiles) issue(t + 1);
+    // this wave's loads of tile t (and the Q loads before them) are done
+    // once at most `ahead` younger tiles of its loads remain in flight; the
+    // barrier publishes every wave's and frees the stage of tile t - 1
+    wait_vm(min(n_tiles - 1 - t, C::STAGES - 2) * C::QW);
+    __builtin_amdgcn_s_barrier();
+    if (t + C::STAGES - 1 < n_tiles) issue(t + C::STAGES - 1);
     const int j0 = j_first + t * AKT;
     if (!wave_any || j0 >= wk_hi || j0 + AKT <= wk_lo) continue;
-    const uint8_t* Ks = smem + (t & 1) * C::TILE;
+    const uint8_t* Ks = smem + (t % C::STAGES) * C::TILE;
     const uint8_t* Vs = Ks + 64 * C::ROWB;
 
     // ---- S^T = K Q^T: lane holds keys 16 mt + 4 g + r of query li ----
@@ -167,29 +172,41 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
       }
     }
 
-    // ---- mask (same text: q_start <= key < q_end; window), online softmax ----
+    // ---- mask, online softmax.  The lane holds keys j0 + 16 mt + 4 g + r
+    // of its query; key kj is allowed iff kj - k_lo < k_span (unsigned).  A
+    // tile whose keys every lane of the wave may all see skips the test ----
     float sv[16];
     float mloc = NEG_INF;
+    const int kb = j0 + 4 * g - k_lo;  // key offset of element (0, 0) from k_lo
+    if (__all((unsigned)kb < k_span && (unsigned)(kb + 51) < k_span)) {
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
+      for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int kj = j0 + 16 * mt + 4 * g + r;
-        const int d = qi - kj;
-        const bool ok = kj >= q_start && kj < q_end && (is_global || (d <= window && -d <= window));
-        sv[mt * 4 + r] = ok ? sacc[mt][r] : NEG_INF;
-        mloc = fmaxf(mloc, sv[mt * 4 + r]);
-      }
+        for (int r = 0; r < 4; ++r) {
+          sv[mt * 4 + r] = sacc[mt][r];
+          mloc = fmaxf(mloc, sv[mt * 4 + r]);
+        }
+    } else {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = (unsigned)(kb + 16 * mt + r) < k_span;
+          sv[mt * 4 + r] = ok ? sacc[mt][r] : NEG_INF;
+          mloc = fmaxf(mloc, sv[mt * 4 + r]);
+        }
+    }
     mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
     const float m_new = fmaxf(m_run, mloc);
     const float m_use = m_new == NEG_INF ? 0.f : m_new;
-    const float alpha = exp2f((m_run - m_use) * scale_log2);
+    // every exponent below is <= 0 (or -inf): the hardware exp2 suffices
+    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
     const float mb = m_use * scale_log2;
     float psum = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      sv[i] = exp2f(__builtin_fmaf(sv[i], scale_log2, -mb));
+      sv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -mb));
       psum += sv[i];
     }
     psum += __shfl_xor(psum, 16, 64);
@@ -299,10 +316,22 @@ void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, v
   if (T <= 0) return;
   const dim3 grid((T + AQ - 1) / AQ, n_heads);
   const float scale_log2 = 0.125f * 1.4426950408889634f;
+  // a double buffer: deeper rings (3 or 4 stages) measured slower on MI355X
+  constexpr int ST = 2;
+  static bool attr_set = false;  // dynamic LDS above 64 KB must be allowed once
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_BF16, ST>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, AttnCfg<P_BF16, ST>::LDS);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_F32, ST>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, AttnCfg<P_F32, ST>::LDS);
+    attr_set = true;
+  }
   if (prec == P_BF16)
-    k_attn<P_BF16><<<grid, 256, 0, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global, window, scale_log2);
+    k_attn<P_BF16, ST><<<grid, 256, AttnCfg<P_BF16, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global,
+                                                                  window, scale_log2);
   else
-    k_attn<P_F32><<<grid, 256, 0, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global, window, scale_log2);
+    k_attn<P_F32, ST><<<grid, 256, AttnCfg<P_F32, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global,
+                                                                window, scale_log2);
 }
 
 void launch_qkv_prep(int prec, const void* qkv_in, void* qk_out, const QkvOut& qo, int T, hipStream_t s) {

@@ -55,7 +55,8 @@ struct Fmt {
 
 // Block of WGM x WGN waves; each wave owns WM x WN MFMA 16x16 output tiles.
 // A K tile is KT bytes of every operand row (128: 32 fp32, 64 bf16 or 128
-// int8; 64: half that, fp32 and bf16 only), one LDS row each.
+// int8; 64 or 256: half or twice that, fp32 and bf16 only), one LDS row
+// each.
 template <int WM, int WN, int PREC, int STAGES_, int WGM, int WGN, int KT_ = 128>
 struct Cfg {
   static constexpr int KT = KT_;
@@ -75,7 +76,7 @@ struct Cfg {
   static_assert(ROWS * KT % 1024 == 0 && Q % NW == 0, "tile rows must split evenly over the waves");
   static_assert(QW * NW * 1024 == ROWS * KT, "the load instructions cover the tile exactly");
   static_assert(PREC != P_I8 || BN == 32 * NW, "int8 scale staging: 32 W rows per wave");
-  static_assert(KT == 128 || (KT == 64 && PREC != P_I8), "K tile of 128 bytes, or 64 for fp32 / bf16");
+  static_assert(KT == 128 || ((KT == 64 || KT == 256) && PREC != P_I8), "K tile of 128 bytes, or 64 / 256 for fp32 / bf16");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -92,29 +93,6 @@ __device__ __forceinline__ int w_row(int r, int nb, int N) {
   } else {
     return nb * BN + r;
   }
-}
-
-// s_waitcnt vmcnt(n), expcnt and lgkmcnt left at their maxima (gfx9
-// encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14).
-__device__ __forceinline__ void wait_vm(int n) {
-  switch (n) {
-#define TTE_W(k) \
-  case k: __builtin_amdgcn_s_waitcnt(0x0F70 | ((k) & 15) | ((((k) >> 4) & 3) << 14)); break;
-    TTE_W(0) TTE_W(1) TTE_W(2) TTE_W(3) TTE_W(4) TTE_W(5) TTE_W(6) TTE_W(7) TTE_W(8) TTE_W(9) TTE_W(10)
-    TTE_W(11) TTE_W(12) TTE_W(13) TTE_W(14) TTE_W(15) TTE_W(16) TTE_W(17) TTE_W(18) TTE_W(19) TTE_W(20)
-#undef TTE_W
-    default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-  }
-}
-
-typedef __attribute__((address_space(3))) void* lds_ptr;
-
-// One direct-to-LDS load: each lane's 16 bytes at g go to LDS l + 16 * lane
-// (l must be the same for the whole wave).  Kept a plain (non-template)
-// function: the builtin inside templated kernels loses the host-side kernel
-// stub in this compiler.
-__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  __builtin_amdgcn_global_load_lds(g, (lds_ptr)l, 16, 0, 0);
 }
 
 // Issue the direct-to-LDS loads of K tile kt into `stage`: QW 1 KB
@@ -168,20 +146,21 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
   // LDS rows are unpadded and the 16-byte chunk c of row r sits in slot
   // c ^ swizzle(r), so that the rows a fragment read touches (16
   // consecutive rows, one chunk) spread over distinct bank groups:
-  //   KT = 128 (8 chunks): swizzle(r) = r & 7;
-  //   KT = 64 (4 chunks):  swizzle(r) = ((r >> 1) ^ (r >> 3)) & 3, which
+  //   KT = 256 (16 chunks): swizzle(r) = r & 15;
+  //   KT = 128 (8 chunks):  swizzle(r) = r & 7;
+  //   KT = 64 (4 chunks):   swizzle(r) = ((r >> 1) ^ (r >> 3)) & 3, which
   //   puts any 8 consecutive rows in 8 distinct slots of a 128-byte window
   //   and 16 consecutive rows in 16 distinct slots of 256 bytes.
   // Load plan: instruction j of this wave fills the 1 KB of LDS rows
   // RPI q .. RPI q + RPI - 1 (q = wid * QW + j); lane -> row RPI q + lane /
   // (KT/16), slot lane % (KT/16), which holds chunk slot ^ swizzle(row).
   constexpr int CPRW = KT / 16, RPI = 1024 / KT;  // chunks per row, rows per load instruction
-  const int lrow = lane / CPRW;  // row within the instruction's rows (= row mod RPI)
-  const int chunk = KT == 128 ? ((lane & 7) ^ lrow) : ((lane & 3) ^ (((lrow >> 1) ^ (lrow >> 3)) & 3));
+  const int lrow = lane / CPRW, slot = lane % CPRW;
   const uint8_t* src[G::QW];
 #pragma unroll
   for (int j = 0; j < G::QW; ++j) {
     const int r = RPI * (wid * G::QW + j) + lrow;
+    const int chunk = slot ^ (KT == 256 ? (r & 15) : KT == 128 ? (r & 7) : (((r >> 1) ^ (r >> 3)) & 3));
     if (r < BM)
       src[j] = A + (size_t)min(m0 + r, M - 1) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
     else
@@ -202,7 +181,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
   for (int p = 0; p < G::STAGES - 1 && p < nk; ++p)
     issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, src, s_src, p, wid, lane, G::ROWS);
 
-  const int swz = KT == 128 ? (li & 7) : (((li >> 1) ^ (li >> 3)) & 3);
+  const int swz = KT == 256 ? li : KT == 128 ? (li & 7) : (((li >> 1) ^ (li >> 3)) & 3);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of tile kt are done once at most `ahead` tiles of
     // its own loads remain in flight; the barrier publishes every wave's
