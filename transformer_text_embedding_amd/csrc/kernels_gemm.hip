@@ -429,14 +429,15 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
 //  * the 4-wave tiles for the 768-wide residual products: 32 x 128 when
 //    there are few tiles and K is short, else 64 x 128 (a third stage for
 //    long K);
-//  * int8 keeps 4-wave tiles (its scale staging feeds 32 W rows per wave):
-//    128 x 128 once there are >= 1024 such tiles.
+//  * int8 (its scale staging feeds 32 W rows per wave) and fp32 (measured
+//    slower with 8 waves: GeGLU at 957 tokens 54% against 64% of the fp32
+//    peak) keep 4-wave tiles: 128 x 128 once there are >= 1024 such tiles.
 enum TileCfg { T32, T64, T64L, T128, T128W8, T256 };
 
 TileCfg pick_tiles(int prec, int epi, int M, int n_cols, int K) {
   const long tiles128 = (long)((M + 127) / 128) * (n_cols / 128);
   const long tiles256 = (long)((M + 255) / 256) * (n_cols / 256);
-  if (prec == P_I8) {
+  if (prec != P_BF16) {
     if (tiles128 >= 1024) return T128;
   } else if (epi == E_RESID) {
     if (M >= 8192 && n_cols % 256 == 0) return T256;
@@ -456,10 +457,10 @@ void launch_prec(int epi, const void* A, const float* a_scale, const void* W, co
     case T32: go_prec<PREC, 1, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
     case T64L: go_prec<PREC, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
     case T128W8:
-      if constexpr (PREC != P_I8) go_prec<PREC, 2, 2, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+      if constexpr (PREC == P_BF16) go_prec<PREC, 2, 2, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
       break;
     case T256:
-      if constexpr (PREC != P_I8) go_prec<PREC, 8, 2, 2, 4>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+      if constexpr (PREC == P_BF16) go_prec<PREC, 8, 2, 2, 4>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
       break;
     default: go_prec<PREC, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
   }
@@ -469,7 +470,7 @@ template <int PREC, int OUT>
 void launch_qkv_prec(const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int K,
                      void* qkv, const QkvOut& qo, hipStream_t s) {
   const int N = 3 * qo.hidden;
-  if constexpr (PREC == P_I8) {
+  if constexpr (PREC != P_BF16) {
     if (pick_tiles(PREC, E_QKV, M, N, K) == T128) go<PREC, E_QKV, OUT, 4, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
     else go<PREC, E_QKV, OUT, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
   } else {
