@@ -11,6 +11,7 @@ from .encoder import (  # noqa: F401
     decode_matrix,
     encode,
     encode_layers,
+    encode_tokens,
     gelu,
     geglu,
     layer_norm,

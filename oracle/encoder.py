@@ -290,9 +290,15 @@ def encode_layers(cfg: dict, w: dict, ids, offsets, n_layers: Optional[int] = No
     return states
 
 
-def encode(cfg: dict, w: dict, ids, offsets) -> np.ndarray:
-    """Unit-norm embeddings [B, H] of the texts of a pack: the layers, the
-    final LayerNorm, mean pooling per text and L2 normalisation."""
+def encode_tokens(cfg: dict, w: dict, ids, offsets) -> np.ndarray:
+    """Per-token output states [T, H]: the layers and the final LayerNorm,
+    before any pooling (the encoder's own per-token output, which the
+    pooling paragraph of section 何が動くか then averages)."""
     x = encode_layers(cfg, w, ids, offsets)[-1]
-    x = layer_norm(x, w["final_norm"], cfg["ln_eps"])
-    return mean_pool_l2(x, offsets)
+    return layer_norm(x, w["final_norm"], cfg["ln_eps"])
+
+
+def encode(cfg: dict, w: dict, ids, offsets) -> np.ndarray:
+    """Unit-norm embeddings [B, H] of the texts of a pack: the per-token
+    states, mean pooling per text and L2 normalisation."""
+    return mean_pool_l2(encode_tokens(cfg, w, ids, offsets), offsets)

@@ -376,8 +376,7 @@ def test_encode_matches_transformers_modernbert():
         # placement, window bound, QKV layout) moves it by more than 1e-3.
         np.testing.assert_allclose(emb[b], e, rtol=0, atol=1e-7)
         # the per-token states agree too (before pooling)
-        own = oracle.layer_norm(oracle.encode_layers(ocfg, w, pack.text(b), [0, pack.offsets[b + 1] - pack.offsets[b]])[-1],
-                                w["final_norm"], cfg.ln_eps)
+        own = oracle.encode_tokens(ocfg, w, pack.text(b), [0, pack.offsets[b + 1] - pack.offsets[b]])
         np.testing.assert_allclose(own, hs, rtol=0, atol=2e-5)
 
 
