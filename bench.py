@@ -82,6 +82,8 @@ def main():
     ap.add_argument("--workload", default="full_bf16_packs2048")
     ap.add_argument("--streams", type=int, default=3,
                     help="concurrent streams, one model each (3 measured best with 4 hardware queues per process)")
+    ap.add_argument("--output", choices=("pooled", "tokens"), default="pooled",
+                    help="pooled unit vectors per text (tte_embed) or per-token states (tte_embed_tokens)")
     ap.add_argument("--split-k", action="store_true",
                     help="TTE_FLAG_SPLIT_K: split the down-projection of short packs (lower single-call latency)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=3000)
@@ -130,15 +132,18 @@ def main():
                               device="cuda:0", shared_from=model, split_k=a.split_k) for _ in range(S - 1)]
     streams = [torch.cuda.Stream(device=dev) for _ in range(S)]
     ids = [torch.from_numpy(p.ids).to(dev) for p in packs]
-    outs = [torch.empty((p.n_texts, cfg.hidden), dtype=torch.float32, device=dev) for p in packs]
+    per_token = a.output == "tokens"
+    outs = [torch.empty((p.n_tokens if per_token else p.n_texts, cfg.hidden), dtype=torch.float32, device=dev)
+            for p in packs]
     offs = [B.int32_array(p.offsets) for p in packs]
     L = B.lib()
+    embed = L.tte_embed_tokens if per_token else L.tte_embed
 
     def step(n_streams):
         for i, p in enumerate(packs):
             k = i % n_streams
-            st = L.tte_embed(models[k].handle, ids[i].data_ptr(), p.n_tokens, offs[i], p.n_texts, outs[i].data_ptr(),
-                             streams[k].cuda_stream)
+            st = embed(models[k].handle, ids[i].data_ptr(), p.n_tokens, offs[i], p.n_texts, outs[i].data_ptr(),
+                       streams[k].cuda_stream)
             if st != 0:
                 B.check(st)
 
@@ -211,7 +216,7 @@ def main():
         "config": {"workload": a.workload, "packs_per_step": len(packs), "tokens_per_step": tokens_per_step,
                    "pack_budget": spec.get("pack_budget"), "layers": cfg.layers, "hidden": cfg.hidden,
                    "heads": cfg.heads, "intermediate": cfg.intermediate, "calls_per_step": len(packs),
-                   "streams": S, "split_k": a.split_k, "single_stream_ms_per_step": round(single_ms, 3) if single_ms else None},
+                   "streams": S, "output": a.output, "split_k": a.split_k, "single_stream_ms_per_step": round(single_ms, 3) if single_ms else None},
         "roofline": roofline,
     }
     if breakdown is not None:

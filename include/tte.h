@@ -136,6 +136,20 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
 tte_status tte_embed(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens,
                      const int32_t* h_offsets, int32_t n_texts, float* d_out, void* stream);
 
+/* Per-token output of the same pass (section 何が動くか, encoder and pooling
+ * paragraphs: the encoder's states after its final LayerNorm, which pooling
+ * would then average): d_out_tokens fp32 [n_tokens, H], row t for token t of
+ * the pack.  Same arguments, validation and stream semantics as tte_embed. */
+tte_status tte_embed_tokens(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens,
+                            const int32_t* h_offsets, int32_t n_texts, float* d_out_tokens, void* stream);
+
+/* Cosine-similarity matrix of the introduction's -sim example: for unit
+ * vectors (tte_embed's output) the cosine is the dot product, so
+ * d_sim fp32 [n, n] = E E^T with E = d_emb fp32 [n, dim] row-major.
+ * dim must be a positive multiple of 16 (else TTE_E_UNSUPPORTED), n <= 65536;
+ * n = 0 is a no-op.  Device buffers, caller-owned, stream-ordered. */
+tte_status tte_similarity(const float* d_emb, int32_t n, int32_t dim, float* d_sim, void* stream);
+
 /* Like tte_embed, but also copies the residual stream after the embedding
  * LayerNorm and after each of the first n_dump layers into
  * d_states (fp32 [n_dump + 1, n_tokens, H]).  If n_dump < n_layers the pass

@@ -117,3 +117,11 @@ def test_create_without_device_reports_device_error(lib):
     st = lib.tte_create(ctypes.byref(cfg), ctypes.byref(w), ctypes.c_void_p(fake), 1 << 40, ctypes.byref(out))
     assert st == B.TTE_E_DEVICE
     assert "device" in B.last_error()
+
+
+def test_similarity_and_token_entry_checks_need_no_gpu(lib):
+    assert lib.tte_similarity(None, 4, 100, None, None) == B.TTE_E_UNSUPPORTED  # dim not a multiple of 16
+    assert lib.tte_similarity(None, -1, 128, None, None) == B.TTE_E_INVALID
+    assert lib.tte_similarity(None, 0, 128, None, None) == B.TTE_OK  # empty: no-op
+    assert lib.tte_similarity(None, 3, 128, None, None) == B.TTE_E_INVALID  # NULL buffers
+    assert lib.tte_embed_tokens(None, None, 0, None, 0, None, None) == B.TTE_E_INVALID  # NULL model

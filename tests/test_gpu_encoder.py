@@ -58,6 +58,41 @@ def tiny_models():
 
 
 @pytest.mark.parametrize("precision", ["fp32", "bf16", "int8"])
+def test_tiny_per_token_output_matches_oracle(tiny_models, precision):
+    """tte_embed_tokens: the final-normed state of every token."""
+    cfg, w, m = tiny_models[precision]
+    pack = ti.make_packs("tiny_fp32")[0]
+    got = host(m.embed_tokens(dev(pack.ids), pack.offsets))
+    ref = oracle.encode_tokens(cfg.as_dict(), w, pack.ids, pack.offsets)
+    cos = row_cosines(got, ref)
+    say(f"  {precision} per-token cos min {cos.min():.8f} max|d| {np.abs(got - ref).max():.2e}")
+    assert cos.min() >= COS_GATE[precision], cos.min()
+    if precision == "fp32":
+        assert np.abs(got - ref).max() <= 1e-4
+    # pooling the per-token output gives tte_embed's vectors
+    pooled = oracle.mean_pool_l2(got, pack.offsets)
+    np.testing.assert_allclose(pooled, host(m.embed_pack(dev(pack.ids), pack.offsets)), atol=1e-6, rtol=0)
+
+
+def test_per_token_output_empty_pack(tiny_models):
+    _, _, m = tiny_models["fp32"]
+    out = m.embed_tokens(dev(np.zeros(0, np.int32)), [0])
+    assert tuple(out.shape) == (0, m.cfg.hidden)
+
+
+def test_similarity_of_embeddings_matches_oracle(tiny_models):
+    """The -sim matrix of a pack's texts, from the library's own vectors,
+    against the oracle's vectors and cosine matrix."""
+    from transformer_text_embedding_amd import similarity
+    cfg, w, m = tiny_models["fp32"]
+    pack = ti.make_packs("tiny_fp32")[0]
+    e = m.embed_pack(dev(pack.ids), pack.offsets)
+    got = host(similarity(e))
+    ref = oracle.cosine_matrix(oracle.encode(cfg.as_dict(), w, pack.ids, pack.offsets))
+    np.testing.assert_allclose(got, ref, atol=1e-6, rtol=0)
+
+
+@pytest.mark.parametrize("precision", ["fp32", "bf16", "int8"])
 def test_tiny_pack_matches_oracle(tiny_models, precision):
     cfg, w, m = tiny_models[precision]
     pack = ti.make_packs("tiny_fp32")[0]
@@ -203,6 +238,26 @@ def test_full_size_matches_oracle(full_models, name, pack_index, split_k):
         got = got[texts]
     cos = _gate(got, ref, cfg.precision)
     say(f"  T={pack.n_tokens} B={pack.n_texts} cos min {cos.min():.7f} max|d| {np.abs(got - ref).max():.2e}")
+
+
+@pytest.mark.parametrize("name,split_k", [("full_fp32_957", False), ("full_bf16_packs2048", False),
+                                          ("full_bf16_packs2048", True), ("full_int8_packs2048", False)])
+def test_full_size_per_token_output_pools_to_embeddings(full_models, name, split_k):
+    """At full size: mean pooling + L2 of tte_embed_tokens's output equals
+    tte_embed's vectors (the same pass up to the final norm), and every
+    per-token state is a LayerNorm output (gain 1: zero mean, unit
+    variance)."""
+    packs = ti.make_packs(name)
+    pack = packs[min(1, len(packs) - 1)]
+    m = full_models(name, split_k)
+    ids = dev(pack.ids)
+    tok = host(m.embed_tokens(ids, pack.offsets))
+    emb = host(m.embed_pack(ids, pack.offsets))
+    assert np.isfinite(tok).all()
+    np.testing.assert_allclose(oracle.mean_pool_l2(tok, pack.offsets), emb, atol=2e-6, rtol=0)
+    np.testing.assert_allclose(tok.mean(axis=1), 0.0, atol=1e-4)
+    # var(LN(x)) = var(x) / (var(x) + eps) with gain 1
+    np.testing.assert_allclose(tok.var(axis=1), 1.0, atol=5e-3)
 
 
 @pytest.mark.parametrize("name,split_k", [("full_fp32_957", False), ("full_bf16_packs2048", False),

@@ -360,6 +360,27 @@ def test_attention(precision, lengths, layer):
 
 
 # --------------------------------------------------------------------------
+# similarity matrix
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("n,dim", [(1, 768), (5, 768), (16, 128), (17, 768), (130, 768), (64, 16)])
+def test_similarity_matrix(n, dim):
+    t = torch()
+    rng = np.random.default_rng(41 * n + dim)
+    e = rng.normal(size=(n, dim))
+    e = (e / np.linalg.norm(e, axis=1, keepdims=True)).astype(np.float32)
+    de = dev(e)
+    sim = empty((n, n), t.float32)
+    B.tte_similarity(de.data_ptr(), n, dim, sim.data_ptr(), stream())
+    got = host(sim)
+    ref = oracle.cosine_matrix(e)
+    # fp32 products and sums of dim terms of size <= 1
+    np.testing.assert_allclose(got, ref, atol=2e-6, rtol=0)
+    np.testing.assert_allclose(np.diag(got), 1.0, atol=2e-6)
+    np.testing.assert_array_equal(got, got.T)  # same products, same order
+
+
+# --------------------------------------------------------------------------
 # pooling
 # --------------------------------------------------------------------------
 

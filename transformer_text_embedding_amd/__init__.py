@@ -13,7 +13,18 @@ import numpy as np
 
 from . import binding as B
 
-__all__ = ["Model", "make_config", "B"]
+__all__ = ["Model", "make_config", "similarity", "B"]
+
+
+def similarity(emb_dev, stream=None):
+    """Cosine-similarity matrix fp32 [n, n] of unit vectors emb_dev fp32
+    [n, dim] (device tensor; dim a multiple of 16)."""
+    import torch
+    n, dim = emb_dev.shape
+    out = torch.empty((n, n), dtype=torch.float32, device=emb_dev.device)
+    st = stream.cuda_stream if stream is not None else torch.cuda.current_stream(emb_dev.device).cuda_stream
+    B.tte_similarity(emb_dev.data_ptr() if n else 0, n, dim, out.data_ptr() if n else 0, st)
+    return out
 
 
 def make_config(spec, max_tokens: int, max_text_len: int, max_texts: Optional[int] = None,
@@ -112,6 +123,17 @@ class Model:
             out = t.empty((max(n_texts, 0), self.cfg.hidden), dtype=t.float32, device=self.device)
         B.tte_embed(self.handle, ids_dev.data_ptr() if ids_dev.numel() else 0, int(ids_dev.numel()), offsets,
                     out.data_ptr() if out.numel() else 0, self._stream(stream))
+        return out
+
+    def embed_tokens(self, ids_dev, offsets: Sequence[int], out=None, stream=None):
+        """Enqueue one pack; returns the per-token output states, fp32 [T, H]
+        (device; the final LayerNorm of every token, no pooling)."""
+        t = self.torch
+        T = int(ids_dev.numel())
+        if out is None:
+            out = t.empty((T, self.cfg.hidden), dtype=t.float32, device=self.device)
+        B.tte_embed_tokens(self.handle, ids_dev.data_ptr() if T else 0, T, offsets, out.data_ptr() if T else 0,
+                           self._stream(stream))
         return out
 
     def trace(self, ids_dev, offsets, n_dump: int, stream=None):

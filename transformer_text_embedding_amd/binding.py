@@ -58,6 +58,8 @@ _SIGS = {
     "tte_op_quant7": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p, c_void_p]),
     "tte_op_gemm": (c_int32, [c_int32, c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                               c_void_p, c_int32, c_void_p]),
+    "tte_embed_tokens": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_void_p, c_void_p]),
+    "tte_similarity": (c_int32, [c_void_p, c_int32, c_int32, c_void_p, c_void_p]),
     "tte_op_gemm_splitk": (c_int32, [c_int32, c_void_p, c_void_p, c_void_p, c_void_p, c_int32, c_int32, c_int32,
                                      c_int32, c_void_p, c_void_p]),
     "tte_op_resid_ln": (c_int32, [c_void_p, c_void_p, c_int32, c_void_p, c_int32, c_int32, c_float, c_int32, c_void_p,
@@ -166,6 +168,16 @@ def tte_op_gemm(precision: int, epilogue: int, d_a: int, d_a_scale: int, d_w: in
     check(lib().tte_op_gemm(precision, epilogue, c_void_p(d_a), c_void_p(d_a_scale) if d_a_scale else None,
                             c_void_p(d_w), c_void_p(d_w_scale) if d_w_scale else None, M, N, K, c_void_p(d_c),
                             out_kind, c_void_p(stream)))
+
+
+def tte_embed_tokens(model: int, d_ids: int, n_tokens: int, offsets, d_out_tokens: int, stream: int) -> None:
+    arr = int32_array(offsets)
+    check(lib().tte_embed_tokens(c_void_p(model), c_void_p(d_ids), n_tokens, arr, len(offsets) - 1,
+                                 c_void_p(d_out_tokens), c_void_p(stream)))
+
+
+def tte_similarity(d_emb: int, n: int, dim: int, d_sim: int, stream: int) -> None:
+    check(lib().tte_similarity(c_void_p(d_emb), n, dim, c_void_p(d_sim), c_void_p(stream)))
 
 
 def tte_op_gemm_splitk(precision: int, d_a: int, d_a_scale: int, d_w: int, d_w_scale: int, M: int, N: int, K: int,

@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libtte.so")
-SOURCES = ["kernels_rows.hip", "kernels_gemm.hip", "kernels_attn.hip", "tte.hip"]
+SOURCES = ["kernels_rows.hip", "kernels_gemm.hip", "kernels_attn.hip", "kernels_sim.hip", "tte.hip"]
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [

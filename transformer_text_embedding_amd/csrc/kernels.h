@@ -83,6 +83,10 @@ void launch_qkv_prep(int prec, const void* qkv_in, void* qk_out, const QkvOut& q
 void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, void* o, const Seg* seg, int T,
                       int n_heads, int is_global, int window, hipStream_t s);
 
+// Cosine-similarity matrix of unit vectors: sim [n, n] = E E^T, E fp32
+// [n, dim] row-major, dim % 16 == 0.
+void launch_similarity(const float* e, int n, int dim, float* sim, hipStream_t s);
+
 // Final LayerNorm + mean per text + L2.  Units of up to POOL_ROWS rows of
 // one text: unit_start[b] .. unit_start[b+1] belong to text b.
 constexpr int POOL_ROWS = 32;

@@ -226,8 +226,11 @@ __global__ void k_seg(const int* __restrict__ off, int n_texts, int T, Seg* __re
   seg[t] = Seg{off[lo], off[lo + 1]};
 }
 
+// One pass over a pack.  The output is either the pooled unit vectors
+// (d_out [B, H]) or, with d_tok, the per-token states after the final
+// LayerNorm ([T, H]).
 tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t* h_off, int32_t B, float* d_out,
-                    float* d_states, int32_t n_dump, void* stream) {
+                    float* d_states, int32_t n_dump, void* stream, float* d_tok = nullptr) {
   if (!m) return fail(TTE_E_INVALID, "model is NULL");
   const tte_config& c = m->cfg;
   tte_status st = check_pack(c, T, h_off, B);
@@ -240,7 +243,7 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
     n_dump = -1;
   }
   const int n_run = (d_states && n_dump < c.n_layers) ? n_dump : c.n_layers;
-  if (n_run == c.n_layers && !d_out) return fail(TTE_E_INVALID, "d_out is NULL");
+  if (n_run == c.n_layers && !d_out && !d_tok) return fail(TTE_E_INVALID, "d_out is NULL");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   st = hip_check(hipSetDevice(m->device), "hipSetDevice");
   if (st != TTE_OK) return st;
@@ -333,7 +336,10 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
     }
     if (d_states) (void)hipMemcpyAsync(d_states + (size_t)(l + 1) * T * H, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
   }
-  if (n_run == c.n_layers) {
+  if (n_run == c.n_layers && d_tok) {
+    ProfScope ps(m, TTE_K_NORM, s);
+    launch_ln(m->x, m->w.final_norm, T, H, c.ln_eps, O_F32, d_tok, nullptr, s);
+  } else if (n_run == c.n_layers) {
     ProfScope ps(m, TTE_K_POOL, s);
     launch_pool(m->x, m->w.final_norm, c.ln_eps, H, m->d_off, m->d_unit, B, n_units, m->partial, d_out, s);
   }
@@ -454,6 +460,23 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
 tte_status tte_embed(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens, const int32_t* h_offsets,
                      int32_t n_texts, float* d_out, void* stream) {
   return run_pass(m, d_token_ids, n_tokens, h_offsets, n_texts, d_out, nullptr, 0, stream);
+}
+
+tte_status tte_embed_tokens(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens, const int32_t* h_offsets,
+                            int32_t n_texts, float* d_out_tokens, void* stream) {
+  if (!d_out_tokens && n_texts > 0) return fail(TTE_E_INVALID, "d_out_tokens is NULL");
+  return run_pass(m, d_token_ids, n_tokens, h_offsets, n_texts, nullptr, nullptr, 0, stream, d_out_tokens);
+}
+
+tte_status tte_similarity(const float* d_emb, int32_t n, int32_t dim, float* d_sim, void* stream) {
+  if (n < 0) return fail(TTE_E_INVALID, "n must be >= 0");
+  if (dim <= 0 || dim % 16 != 0) return fail(TTE_E_UNSUPPORTED, "dim must be a positive multiple of 16");
+  if (n > 65536) return fail(TTE_E_UNSUPPORTED, "n above 65536");
+  if (n == 0) return TTE_OK;
+  if (!d_emb || !d_sim) return fail(TTE_E_INVALID, "NULL buffer");
+  (void)hipGetLastError();
+  launch_similarity(d_emb, n, dim, d_sim, reinterpret_cast<hipStream_t>(stream));
+  return hip_check(hipGetLastError(), "kernel launch");
 }
 
 tte_status tte_embed_trace(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens, const int32_t* h_offsets,
