@@ -256,32 +256,61 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
   if constexpr (EPI == E_QKV) {
     static_assert(WN == 4, "QKV epilogue: a wave's 64 columns are one head");
     const int n_base = nb * BN + wn * 64;
+    constexpr int RBQ = 64 * 4 + 16;
+    static_assert(G::NW * 16 * RBQ <= G::LDS, "staging fits the K-tile ring");
+    __syncthreads();  // every wave is done with the K-tile ring
     if (n_base < 2 * qo.hidden) {
-      // Q or K: rotate the pairs (d, d + 32), d = 16 nt + li, nt = 0, 1
+      // Q or K: the wave's 16-row slabs pass through LDS in fp32 (rows padded
+      // by 16 bytes); then lane (row = lane / 4, c = lane % 4) rotates the
+      // pairs (d, d + 32) for d = 8c .. 8c + 7 of its row with 16-byte table
+      // reads and writes 16-byte vectors of the rotated dims.
+      uint8_t* slab = smem + wid * 16 * RBQ;
+      const int row = lane >> 2, c = lane & 3;
 #pragma unroll
-      for (int mt = 0; mt < WM; ++mt)
+      for (int mt = 0; mt < WM; ++mt) {
+        const int m_slab = m0 + wm * 16 * WM + mt * 16;
+        float rs[4] = {1.f, 1.f, 1.f, 1.f};
+        if constexpr (PREC == P_I8) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int m = m0 + wm * 16 * WM + mt * 16 + 4 * g + r;
-          if (m >= M) continue;
-          float rs = 1.f;
-          if constexpr (PREC == P_I8) rs = a_scale[m];
+          for (int r = 0; r < 4; ++r) rs[r] = a_scale[min(m_slab + 4 * g + r, M - 1)];
+        }
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            *reinterpret_cast<float*>(slab + (4 * g + r) * RBQ + (nt * 16 + li) * 4) = acc[mt][nt][r] * rs[r];
+        // LDS operations of one wave complete in order
+        __builtin_amdgcn_wave_barrier();
+        const int m = m_slab + row;
+        if (m < M) {
+          const float* xs = reinterpret_cast<const float*>(slab + row * RBQ) + 8 * c;
+          const f32x4 x0 = *reinterpret_cast<const f32x4*>(xs), x1 = *reinterpret_cast<const f32x4*>(xs + 4);
+          const f32x4 y0 = *reinterpret_cast<const f32x4*>(xs + 32), y1 = *reinterpret_cast<const f32x4*>(xs + 36);
           const int pos = m - qo.seg[m].start;
-#pragma unroll
-          for (int nt = 0; nt < 2; ++nt) {
-            const int d = nt * 16 + li;
-            const float c = qo.cos_tab[pos * 32 + d], sn = qo.sin_tab[pos * 32 + d];
-            const float x = acc[mt][nt][r] * rs, y = acc[mt][nt + 2][r] * rs;
-            const float xr = x * c - y * sn, yr = y * c + x * sn;
-            if constexpr (OUT == O_BF16) {
-              reinterpret_cast<uint16_t*>(C)[(size_t)m * N + n_base + d] = f32_to_bf16(xr);
-              reinterpret_cast<uint16_t*>(C)[(size_t)m * N + n_base + d + 32] = f32_to_bf16(yr);
-            } else {
-              reinterpret_cast<float*>(C)[(size_t)m * N + n_base + d] = xr;
-              reinterpret_cast<float*>(C)[(size_t)m * N + n_base + d + 32] = yr;
-            }
+          const float* ct = qo.cos_tab + pos * 32 + 8 * c;
+          const float* st = qo.sin_tab + pos * 32 + 8 * c;
+          const f32x4 c0 = *reinterpret_cast<const f32x4*>(ct), c1 = *reinterpret_cast<const f32x4*>(ct + 4);
+          const f32x4 s0 = *reinterpret_cast<const f32x4*>(st), s1 = *reinterpret_cast<const f32x4*>(st + 4);
+          const f32x4 xr0 = x0 * c0 - y0 * s0, xr1 = x1 * c1 - y1 * s1;
+          const f32x4 yr0 = y0 * c0 + x0 * s0, yr1 = y1 * c1 + x1 * s1;
+          const size_t at = (size_t)m * N + n_base + 8 * c;
+          if constexpr (OUT == O_BF16) {
+            const u32x4 px = {pack_bf16x2(xr0[0], xr0[1]), pack_bf16x2(xr0[2], xr0[3]), pack_bf16x2(xr1[0], xr1[1]),
+                              pack_bf16x2(xr1[2], xr1[3])};
+            const u32x4 py = {pack_bf16x2(yr0[0], yr0[1]), pack_bf16x2(yr0[2], yr0[3]), pack_bf16x2(yr1[0], yr1[1]),
+                              pack_bf16x2(yr1[2], yr1[3])};
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + at) = px;
+            *reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(C) + at + 32) = py;
+          } else {
+            float* cp = reinterpret_cast<float*>(C) + at;
+            *reinterpret_cast<f32x4*>(cp) = xr0;
+            *reinterpret_cast<f32x4*>(cp + 4) = xr1;
+            *reinterpret_cast<f32x4*>(cp + 32) = yr0;
+            *reinterpret_cast<f32x4*>(cp + 36) = yr1;
           }
         }
+        __builtin_amdgcn_wave_barrier();
+      }
     } else {
       // V: transposed, the lane's 4 consecutive tokens of one column at once
 #pragma unroll
@@ -406,17 +435,17 @@ void go(const void* A, const float* a_scale, const void* W, const float* w_scale
                                                  m_blocks, splits, qo);
 }
 
-template <int PREC, int WM, int ST, int WGM = 2, int WGN = 2>
+template <int PREC, int WM, int ST, int WGM = 2, int WGN = 2, int KT = 128>
 void go_prec(int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N, int K,
              void* C, int out_kind, hipStream_t s) {
   if (epi == E_RESID) {
-    go<PREC, E_RESID, O_F32, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
+    go<PREC, E_RESID, O_F32, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
   } else if (epi == E_GEGLU) {
-    if (out_kind == O_BF16) go<PREC, E_GEGLU, O_BF16, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
-    else go<PREC, E_GEGLU, O_F32, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
+    if (out_kind == O_BF16) go<PREC, E_GEGLU, O_BF16, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
+    else go<PREC, E_GEGLU, O_F32, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
   } else {
-    if (out_kind == O_BF16) go<PREC, E_STORE, O_BF16, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
-    else go<PREC, E_STORE, O_F32, WM, 4, ST, WGM, WGN>(A, a_scale, W, w_scale, M, N, K, C, s);
+    if (out_kind == O_BF16) go<PREC, E_STORE, O_BF16, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
+    else go<PREC, E_STORE, O_F32, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
   }
 }
 
@@ -427,8 +456,10 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
 //  * T128W8: 128 x 128, 8 waves of 32 x 64 (two blocks per CU): the other
 //    wide products (QKV always, GeGLU below the T256 size);
 //  * the 4-wave tiles for the 768-wide residual products: 32 x 128 when
-//    there are few tiles and K is short, else 64 x 128 (a third stage for
-//    long K);
+//    there are few tiles and K is short, else 64 x 128, with a third stage
+//    for long K (256-byte K tiles measured faster for the down-projection
+//    alone, 351 against 324 TFLOP/s at 1.9k rows, but slower inside the
+//    pass, 33.4 against 29.1 us per launch, and are not dispatched);
 //  * int8 (its scale staging feeds 32 W rows per wave) and fp32 (measured
 //    slower with 8 waves: GeGLU at 957 tokens 54% against 64% of the fp32
 //    peak) keep 4-wave tiles: 128 x 128 once there are >= 1024 such tiles.
