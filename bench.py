@@ -51,6 +51,44 @@ def traffic_from_profile(kernel_source: str, profile: str):
     return meta["per_launch_mean"]["traffic_bytes"]
 
 
+HBM_GBS = 8000.0
+
+
+def allowed_pairs(lengths, window):
+    """(query, key) pairs attention computes: global layers see the whole
+    text, local ones keys at most `window` positions away."""
+    lengths = [int(L) for L in lengths]  # Python ints: the totals overflow int32
+    g = sum(L * L for L in lengths)
+    loc = 0
+    for L in lengths:
+        i = np.arange(L)
+        loc += int(np.sum(np.minimum(L, i + window + 1) - np.maximum(0, i - window)))
+    return g, loc
+
+
+def class_work(cfg, packs):
+    """Algorithmic work of one step per kernel class: (amount, unit, peak).
+    GEMMs 2 N K flops per token; attention 4 * head_dim flops per allowed
+    pair per head; the row kernels the bytes they must read and write."""
+    H, I, Lyr = cfg.hidden, cfg.intermediate, cfg.layers
+    T = sum(p.n_tokens for p in packs)
+    gemm_peak = PEAK_TFLOPS[cfg.precision]
+    attn_peak = PEAK_TFLOPS["bf16"] if cfg.precision == "bf16" else PEAK_TFLOPS["fp32"]
+    n_glob = len([l for l in range(Lyr) if l % cfg.global_every == 0])
+    pg = pl = 0
+    for p in packs:
+        g, loc = allowed_pairs(np.diff(p.offsets), cfg.window)
+        pg, pl = pg + g, pl + loc
+    per_pair = 4 * cfg.head_dim * cfg.heads
+    out_b = {"bf16": 2, "fp32": 4, "int8": 1}[cfg.precision]
+    w = {k: (f(H, I) * T * Lyr, "TFLOP/s", gemm_peak) for k, f in GEMM_CLASSES.items()}
+    w["attn_global"] = (pg * per_pair * n_glob, "TFLOP/s", attn_peak)
+    w["attn_local"] = (pl * per_pair * (Lyr - n_glob), "TFLOP/s", attn_peak)
+    w["norm"] = (2 * Lyr * T * H * (4 + out_b), "GB/s", None)  # read fp32 rows, write the GEMM operand
+    w["pool"] = (T * H * 4, "GB/s", None)
+    return w
+
+
 def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
@@ -199,13 +237,20 @@ def main():
         step(1)
         prof = B.tte_profile_stop(h)
         breakdown = {}
+        work = class_work(cfg, packs)
         for k, (ms, n) in prof.items():
             if n == 0:
                 continue
             entry = {"ms": round(ms, 3), "launches": int(n)}
-            if k in GEMM_CLASSES:
-                tf = GEMM_CLASSES[k](H, I) * tokens_per_step * cfg.layers / (ms / 1e3) / 1e12
-                entry["TFLOP/s"] = round(tf, 1)
+            if k in work:
+                amount, unit, peak = work[k]
+                rate = amount / (ms / 1e3)
+                if unit == "TFLOP/s":
+                    entry["TFLOP/s"] = round(rate / 1e12, 1)
+                    entry["frac_of_peak"] = round(rate / 1e12 / peak, 4)
+                else:
+                    entry["GB/s"] = round(rate / 1e9, 1)
+                    entry["frac_of_hbm"] = round(rate / 1e9 / HBM_GBS, 4)
             breakdown[k] = entry
 
     torch.cuda.synchronize()

@@ -33,17 +33,37 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
+// Wave-wide sum / max, returned to every lane.  DPP lane moves (no LDS
+// round trip): swaps within quads, the half-row and row mirrors give every
+// lane its 16-lane row's result; row_bcast:15 and row_bcast:31 (gfx9) then
+// fold rows 0..3 into lane 63, which readlane broadcasts.  The combining
+// order is fixed, so results are deterministic.  `id` is the operation's
+// identity, which lanes of rows a broadcast step leaves out receive.
+#define TTE_DPP(x, ctrl, row_mask, id)                                                                          \
+  __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(id), __float_as_int(x), (ctrl), (row_mask), 0xF, \
+                                             false))
+
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, WAVE);
-  return v;
+  v += TTE_DPP(v, 0xB1, 0xF, 0.f);   // quad_perm [1, 0, 3, 2]
+  v += TTE_DPP(v, 0x4E, 0xF, 0.f);   // quad_perm [2, 3, 0, 1]
+  v += TTE_DPP(v, 0x141, 0xF, 0.f);  // row_half_mirror
+  v += TTE_DPP(v, 0x140, 0xF, 0.f);  // row_mirror
+  v += TTE_DPP(v, 0x142, 0xA, 0.f);  // row_bcast:15 into rows 1 and 3
+  v += TTE_DPP(v, 0x143, 0xC, 0.f);  // row_bcast:31 into rows 2 and 3
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
 
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, WAVE));
-  return v;
+  const float id = -__builtin_huge_valf();
+  v = fmaxf(v, TTE_DPP(v, 0xB1, 0xF, id));
+  v = fmaxf(v, TTE_DPP(v, 0x4E, 0xF, id));
+  v = fmaxf(v, TTE_DPP(v, 0x141, 0xF, id));
+  v = fmaxf(v, TTE_DPP(v, 0x140, 0xF, id));
+  v = fmaxf(v, TTE_DPP(v, 0x142, 0xA, id));
+  v = fmaxf(v, TTE_DPP(v, 0x143, 0xC, id));
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
 }
+#undef TTE_DPP
 
 // 7-bit row code: clamp(rint(x * inv), -63, 63) with ties to even.
 __device__ __forceinline__ int quant7(float x, float inv) {

@@ -103,6 +103,8 @@ template <int EPL>
 __device__ __forceinline__ void layernorm_regs(float (&v)[EPL], const float* __restrict__ gamma, int lane,
                                                float eps) {
   using RS = RowShape<EPL>;
+  float g[EPL];
+  load_f32_row<EPL>(gamma, lane, g);  // issued before the reductions
   float s = 0.f;
 #pragma unroll
   for (int i = 0; i < EPL; ++i) s += v[i];
@@ -113,9 +115,7 @@ __device__ __forceinline__ void layernorm_regs(float (&v)[EPL], const float* __r
     v[i] -= mean;
     q += v[i] * v[i];
   }
-  const float rstd = 1.f / sqrtf(wave_sum(q) * (1.f / RS::W) + eps);
-  float g[EPL];
-  load_f32_row<EPL>(gamma, lane, g);
+  const float rstd = __builtin_amdgcn_rsqf(wave_sum(q) * (1.f / RS::W) + eps);
 #pragma unroll
   for (int i = 0; i < EPL; ++i) v[i] = v[i] * rstd * g[i];
 }
