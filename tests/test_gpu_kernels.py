@@ -82,8 +82,9 @@ def test_layernorm_to_int8_codes():
 # fp32 / bf16 products) and 256x256 (>= 512 such tiles, or residual
 # products of >= 8k rows)
 SHAPES = [(178, 384, 128), (957, 2304, 768), (300, 768, 3072), (130, 512, 256), (1, 128, 128), (4100, 4096, 128),
-          (8200, 768, 3072)]
-GEGLU_SHAPES = [(178, 256, 128), (957, 3072, 768), (65, 64, 256), (2100, 4096, 128), (8192, 3072, 768)]
+          (8200, 768, 3072), (1913, 2304, 768)]
+GEGLU_SHAPES = [(178, 256, 128), (957, 3072, 768), (65, 64, 256), (2100, 4096, 128), (8192, 3072, 768),
+                (1913, 3072, 768)]
 
 
 def _run_gemm(prec, epi, a, a_s, w, w_s, M, N, K, c, out_kind):
@@ -408,7 +409,8 @@ def test_pool(lengths):
 # --------------------------------------------------------------------------
 
 @pytest.mark.parametrize("precision", ["fp32", "bf16", "int8"])
-@pytest.mark.parametrize("lengths", [[8, 40, 130], [1, 64, 65, 300, 3]])
+# 178 and 433 tokens take the 128-row tiles, 1913 the 192-row ones (bf16)
+@pytest.mark.parametrize("lengths", [[8, 40, 130], [1, 64, 65, 300, 3], [500, 700, 713]])
 @pytest.mark.parametrize("layer", [0, 1])
 def test_qkv_rope_epilogue(precision, lengths, layer):
     t = torch()

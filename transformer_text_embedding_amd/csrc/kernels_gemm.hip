@@ -453,8 +453,13 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
 // 16k tokens; 2 LDS stages of 128-byte K tiles unless noted):
 //  * T256: 256 x 256, 8 waves of 128 x 64 (one block per CU): wide products
 //    with >= 512 such tiles, and the residual products of >= 8k rows;
-//  * T128W8: 128 x 128, 8 waves of 32 x 64 (two blocks per CU): the other
-//    wide products (QKV always, GeGLU below the T256 size);
+//  * T128W8 / T192W8: 128 x 128 or 192 x 128, 8 waves of 32 x 64 or
+//    48 x 64 (two blocks per CU): the other wide products (QKV always,
+//    GeGLU below the T256 size).  The height is the one with the smaller
+//    ceil(tiles / 256) * rows, a count of tile-rows the busiest CU works
+//    through (ties to 192: fewer tiles re-read A less): at 1.9k rows GeGLU
+//    runs 803 against 739 TFLOP/s in 192-row tiles, at 2048 rows 651
+//    against 771;
 //  * the 4-wave tiles for the 768-wide residual products: 32 x 128 when
 //    there are few tiles and K is short, else 64 x 128, with a third stage
 //    for long K (256-byte K tiles measured faster for the down-projection
@@ -463,7 +468,7 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
 //  * int8 (its scale staging feeds 32 W rows per wave) and fp32 (measured
 //    slower with 8 waves: GeGLU at 957 tokens 54% against 64% of the fp32
 //    peak) keep 4-wave tiles: 128 x 128 once there are >= 1024 such tiles.
-enum TileCfg { T32, T64, T64L, T128, T128W8, T256 };
+enum TileCfg { T32, T64, T64L, T128, T128W8, T192W8, T256 };
 
 TileCfg pick_tiles(int prec, int epi, int M, int n_cols, int K) {
   const long tiles128 = (long)((M + 127) / 128) * (n_cols / 128);
@@ -474,7 +479,9 @@ TileCfg pick_tiles(int prec, int epi, int M, int n_cols, int K) {
     if (M >= 8192 && n_cols % 256 == 0) return T256;
   } else {
     if (tiles256 >= 512 && n_cols % 256 == 0) return T256;
-    return T128W8;
+    const long c128 = ((tiles128 + 255) / 256) * 128;
+    const long c192 = (((long)((M + 191) / 192) * (n_cols / 128) + 255) / 256) * 192;
+    return c192 <= c128 ? T192W8 : T128W8;
   }
   if (tiles128 < 256 && n_cols <= 1024 && K <= 1024) return T32;
   return K > 1024 ? T64L : T64;
@@ -490,6 +497,9 @@ void launch_prec(int epi, const void* A, const float* a_scale, const void* W, co
     case T128W8:
       if constexpr (PREC == P_BF16) go_prec<PREC, 2, 2, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
       break;
+    case T192W8:
+      if constexpr (PREC == P_BF16) go_prec<PREC, 3, 2, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+      break;
     case T256:
       if constexpr (PREC == P_BF16) go_prec<PREC, 8, 2, 2, 4>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
       break;
@@ -504,6 +514,8 @@ void launch_qkv_prec(const void* A, const float* a_scale, const void* W, const f
   if constexpr (PREC != P_BF16) {
     if (pick_tiles(PREC, E_QKV, M, N, K) == T128) go<PREC, E_QKV, OUT, 4, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
     else go<PREC, E_QKV, OUT, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+  } else if (pick_tiles(PREC, E_QKV, M, N, K) == T192W8) {
+    go<PREC, E_QKV, OUT, 3, 4, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
   } else {
     go<PREC, E_QKV, OUT, 2, 4, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
   }
