@@ -40,6 +40,9 @@
 // columns are up-projection rows n (the GELU half) and the second half rows
 // I + n (the gate half): the two halves of one output land in the same lane
 // and combine in registers, and the [M, 2I] intermediate is never stored.
+#include <algorithm>
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -112,7 +115,7 @@ template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES, int WGM, int W
 __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
                                               const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
                                               void* __restrict__ C, int M, int N, int K, int n_blocks,
-                                              int m_blocks, int splits, QkvOut qo) {
+                                              int m_blocks, int grp, int splits, QkvOut qo) {
   using F = Fmt<PREC>;
   using G = Cfg<WM, WN, PREC, STAGES, WGM, WGN, KT>;
   constexpr int BM = G::BM, BN = G::BN;
@@ -124,17 +127,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
   const int g = lane >> 4, li = lane & 15;
 
   // XCD-aware tile order: block b runs on XCD b mod 8; XCD x gets a
-  // contiguous run of a grouped order (groups of n_blocks/4 column
-  // blocks, every row block inside a group).  A run of n_tiles/8 tiles then
-  // spans about half of A's rows and a quarter of W's, which together fit
-  // that XCD's L2.
+  // contiguous run of a grouped order (groups of `grp` column blocks, every
+  // row block inside a group), so its n_tiles/8 tiles cover about
+  // (n_tiles/8)/grp row blocks by grp column blocks of the product; the
+  // host picks grp to balance the A rows and W rows that run reads.
   const int n_tiles = n_blocks * m_blocks;
   // split-K: block b computes K part b / n_tiles of tile b % n_tiles
   const int split = blockIdx.x / n_tiles, tile_bid = blockIdx.x - split * n_tiles;
   const int xcd = tile_bid & 7, local = tile_bid >> 3;
   const int per = n_tiles >> 3, extra = n_tiles & 7;
   const int tile = xcd * per + min(xcd, extra) + local;
-  const int grp = max(1, n_blocks >> 2);
   const int ng = tile / (m_blocks * grp), gbase = ng * grp, gwidth = min(grp, n_blocks - gbase);
   const int grem = tile - ng * m_blocks * grp;
   const int mb = grem / gwidth, nb = gbase + grem % gwidth;
@@ -430,9 +432,14 @@ void go(const void* A, const float* a_scale, const void* W, const float* w_scale
   }
   const int n_blocks = EPI == E_GEGLU ? N / (G::BN / 2) : N / G::BN;
   const int m_blocks = (M + G::BM - 1) / G::BM;
+  // group width: an XCD's run of per = tiles/8 tiles reads about
+  // (per/grp) BM rows of A and grp BN rows of W; their sum is least at
+  // grp = sqrt(per BM / BN)
+  const double per = (double)n_blocks * m_blocks / 8.0;
+  const int grp = std::max(1, std::min(n_blocks, (int)std::lround(std::sqrt(per * G::BM / G::BN))));
   k_gemm<PREC, EPI, OUT, WM, WN, STAGES, WGM, WGN, KT><<<n_blocks * m_blocks * splits, G::THREADS, G::LDS, s>>>(reinterpret_cast<const uint8_t*>(A), a_scale,
                                                  reinterpret_cast<const uint8_t*>(W), w_scale, C, M, N, K, n_blocks,
-                                                 m_blocks, splits, qo);
+                                                 m_blocks, grp, splits, qo);
 }
 
 template <int PREC, int WM, int ST, int WGM = 2, int WGN = 2, int KT = 128>
