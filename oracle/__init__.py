@@ -7,6 +7,7 @@ side; both read the same seeded inputs.
 from .encoder import (  # noqa: F401
     attention,
     block_matmul_int8,
+    block_matmul_q4,
     cosine_matrix,
     decode_matrix,
     encode,
@@ -17,6 +18,8 @@ from .encoder import (  # noqa: F401
     layer_norm,
     mean_pool_l2,
     positions,
+    q4_block_params,
+    q4_codes,
     quantize_rows_7bit,
     rope,
     rope_inverse_frequencies,

@@ -229,6 +229,49 @@ def block_matmul_int8(qx: np.ndarray, sx: np.ndarray, qw: np.ndarray, sw: np.nda
     return np.asarray(sx, np.float64)[:, None] * (qx.astype(np.float64) @ wdeq.T)
 
 
+def q4_codes(codes: np.ndarray) -> np.ndarray:
+    """4-bit codes [N, K] from their packed bytes [N, K/2] (two per byte, the
+    even input in the low nibble)."""
+    c = np.asarray(codes, np.uint8)
+    q = np.empty((c.shape[0], 2 * c.shape[1]), np.int64)
+    q[:, 0::2] = c & 15
+    q[:, 1::2] = c >> 4
+    return q
+
+
+def q4_block_params(meta: np.ndarray):
+    """Per 32-input block of a 4-bit matrix: its scale es = fp32(d * sc) and
+    offset eo = fp32(dmin * mn).  meta is uint8 [N, K/128, 16]: per 128
+    inputs the four blocks' 6-bit sc and mn (a byte each), then the fp32 d
+    and dmin of their 256-input super-block.  Returns (es, eo) fp32
+    [N, K/32]."""
+    m = np.ascontiguousarray(meta, np.uint8)
+    N, G, _ = m.shape
+    sc = m[:, :, 0:4].astype(np.float32).reshape(N, 4 * G)
+    mn = m[:, :, 4:8].astype(np.float32).reshape(N, 4 * G)
+    d = np.ascontiguousarray(m[:, :, 8:12]).view("<f4").reshape(N, G)
+    dmin = np.ascontiguousarray(m[:, :, 12:16]).view("<f4").reshape(N, G)
+    es = (np.repeat(d, 4, axis=1) * sc).astype(np.float32)
+    eo = (np.repeat(dmin, 4, axis=1) * mn).astype(np.float32)
+    return es, eo
+
+
+def block_matmul_q4(qx: np.ndarray, sx: np.ndarray, codes: np.ndarray, meta: np.ndarray,
+                    block: int = 32) -> np.ndarray:
+    """The -q4 integer product (section 精度と量子化): 7-bit activation codes
+    against 4-bit weight codes, per block b
+        y[m,n] = sx[m] * sum_b (es[n,b] * P[m,n,b] - eo[n,b] * S[m,b]),
+    P = sum_{k in b} qx[m,k] q[n,k] and S = sum_{k in b} qx[m,k].
+    Evaluated in fp64 as sx * (qx @ W^T) with W = es * q - eo (each term
+    exact in fp64), i.e. the definition up to fp64 summation order."""
+    q = q4_codes(codes)
+    N, K = q.shape
+    es, eo = q4_block_params(meta)
+    wdeq = (q.astype(np.float64).reshape(N, K // block, block) * es.astype(np.float64)[:, :, None]
+            - eo.astype(np.float64)[:, :, None]).reshape(N, K)
+    return np.asarray(sx, np.float64)[:, None] * (qx.astype(np.float64) @ wdeq.T)
+
+
 # --------------------------------------------------------------------------
 # weights in their storage formats
 # --------------------------------------------------------------------------
@@ -246,15 +289,27 @@ def decode_matrix(w: dict, name: str, precision: str) -> np.ndarray:
         N, K = q.shape
         return (q.astype(np.float64).reshape(N, K // 32, 32)
                 * np.asarray(s, np.float64)[:, :, None]).reshape(N, K)
+    if precision == "int4":
+        if name == "tok_emb":  # the token table stays in int8 blocks
+            return decode_matrix(w, name, "int8")
+        q = q4_codes(w[name + "_q4"])
+        N, K = q.shape
+        es, eo = q4_block_params(w[name + "_q4m"])
+        return (q.astype(np.float64).reshape(N, K // 32, 32) * es.astype(np.float64)[:, :, None]
+                - eo.astype(np.float64)[:, :, None]).reshape(N, K)
     raise ValueError(precision)
 
 
 def _project(x: np.ndarray, layer: dict, name: str, precision: str) -> np.ndarray:
-    """x @ W^T for one stored weight.  In int8 mode x is first rounded per row
-    to 7 bits and the block-scaled integer product is taken."""
+    """x @ W^T for one stored weight.  In int8 and int4 modes x is first
+    rounded per row to 7 bits and the block-scaled integer product is
+    taken."""
     if precision == "int8":
         qx, sx = quantize_rows_7bit(x)
         return block_matmul_int8(qx, sx, layer[name + "_q"], layer[name + "_s"])
+    if precision == "int4":
+        qx, sx = quantize_rows_7bit(x)
+        return block_matmul_q4(qx, sx, layer[name + "_q4"], layer[name + "_q4m"])
     return np.asarray(x, np.float64) @ decode_matrix(layer, name, precision).T
 
 

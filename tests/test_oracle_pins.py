@@ -407,3 +407,85 @@ def test_encode_rejects_bad_ids():
     cfg, w32, pack = _tiny_inputs()
     with pytest.raises(ValueError):
         oracle.encode(cfg.as_dict(), w32, np.array([1, 5000, 2]), [0, 3])
+
+
+# --------------------------------------------------------------------------
+# the 4-bit weight path (section 精度と量子化, -q4)
+# --------------------------------------------------------------------------
+
+def test_q4_decode_hand_computed():
+    """One 128-input group, values worked by hand: w = d*sc*q - dmin*mn."""
+    import struct
+    codes = np.zeros((1, 128), np.uint8)
+    codes[0, 0] = 0x21            # inputs 0, 1: q = 1, 2
+    codes[0, 16] = 0xF0           # inputs 32, 33 (block 1): q = 0, 15
+    meta = np.zeros((1, 2, 16), np.uint8)  # K = 256: two groups of 128
+    for g in range(2):
+        meta[0, g, 0:4] = [3, 1, 0, 63]    # sc of blocks 0..3
+        meta[0, g, 4:8] = [5, 2, 0, 1]     # mn
+        meta[0, g, 8:16] = np.frombuffer(struct.pack("<ff", 0.5, 0.25), np.uint8)
+    w = oracle.decode_matrix({"m_q4": codes, "m_q4m": meta}, "m", "int4")
+    assert w.shape == (1, 256)
+    assert w[0, 0] == 0.5 * 3 * 1 - 0.25 * 5 == 0.25
+    assert w[0, 1] == 0.5 * 3 * 2 - 1.25 == 1.75
+    assert w[0, 2] == -1.25                 # q = 0 in block 0
+    assert w[0, 32] == -0.5 and w[0, 33] == 0.5 * 1 * 15 - 0.5 == 7.0
+    assert w[0, 64] == 0.0                  # sc = mn = 0
+    assert w[0, 96] == -0.25                # block 3: q = 0, offset 0.25
+    assert w[0, 128] == -1.25               # second group: same metadata, codes 0
+
+
+def test_q4_quantizer_rounds_to_the_nearest_code():
+    """Quantising N(0, 0.02) weights: every unclipped weight decodes to
+    within half a step es/2 of itself, and clipping is rare."""
+    rng = np.random.default_rng(7)
+    w = rng.normal(0, 0.02, size=(64, 512)).astype(np.float32)
+    codes, meta = ti.quantize_weight_q4(w)
+    back = oracle.decode_matrix({"m_q4": codes, "m_q4m": meta}, "m", "int4")
+    es, eo = oracle.q4_block_params(meta)
+    step = np.repeat(es.astype(np.float64), 32, axis=1)
+    q = oracle.q4_codes(codes)
+    err = np.abs(back - w)
+    inside = (q > 0) & (q < 15)
+    assert np.all(err[inside] <= step[inside] / 2 * (1 + 1e-6))
+    assert np.mean(err <= step / 2 * (1 + 1e-6)) > 0.99
+    cos = np.sum(back * w) / np.linalg.norm(back) / np.linalg.norm(w)
+    assert cos > 0.99
+
+
+def test_block_matmul_q4_exact_block_sums():
+    """The product against its definition with integer block sums P and S
+    and exact rational arithmetic (Fraction of every fp32 scale)."""
+    from fractions import Fraction
+    rng = np.random.default_rng(9)
+    M, N, K = 3, 4, 256
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    qx, sx = oracle.quantize_rows_7bit(x)
+    codes, meta = ti.quantize_weight_q4(rng.normal(0, 0.05, size=(N, K)).astype(np.float32))
+    q = oracle.q4_codes(codes)
+    es, eo = oracle.q4_block_params(meta)
+    got = oracle.block_matmul_q4(qx, sx, codes, meta)
+    for m in range(M):
+        for n in range(N):
+            tot = Fraction(0)
+            for b in range(K // 32):
+                ks = slice(32 * b, 32 * b + 32)
+                P = int(np.dot(qx[m, ks].astype(np.int64), q[n, ks]))
+                S = int(qx[m, ks].astype(np.int64).sum())
+                tot += Fraction(float(es[n, b])) * P - Fraction(float(eo[n, b])) * S
+            exact = float(Fraction(float(sx[m])) * tot)
+            assert abs(got[m, n] - exact) <= 1e-12 * max(1.0, abs(exact))
+
+
+def test_encode_int4_stays_close_to_fp32():
+    """The whole pass with 4-bit layer weights keeps every text's direction
+    (quantisation noise only)."""
+    base = ti.EncoderConfig("small_q4", precision="fp32", seed=3, **ti.SMALL_Q4)
+    w32 = ti.make_fp32_weights(base)
+    q4 = ti.EncoderConfig("small_q4", precision="int4", seed=3, **ti.SMALL_Q4)
+    w4 = ti.storage_weights(q4, w32)
+    pack = ti.random_pack(np.random.default_rng(1), [5, 40, 90], base.vocab)
+    e32 = oracle.encode(base.as_dict(), ti.storage_weights(base, w32), pack.ids, pack.offsets)
+    e4 = oracle.encode(q4.as_dict(), w4, pack.ids, pack.offsets)
+    cos = np.sum(e32 * e4, axis=1)
+    assert cos.min() > 0.95, cos

@@ -37,7 +37,7 @@ class EncoderConfig:
     head_dim: int
     intermediate: int
     layers: int
-    precision: str  # "fp32" | "bf16" | "int8"
+    precision: str  # "fp32" | "bf16" | "int8" | "int4"
     seed: int
     global_every: int = 3
     window: int = 64
@@ -66,7 +66,13 @@ WORKLOADS = {
                              lengths=[4096, 4096, 4096, 4096]),
     "full_int8_packs2048": dict(cfg=EncoderConfig("full_int8_packs2048", precision="int8", seed=4, **FULL),
                                 n_packs=64, pack_budget=2048, len_lo=8, len_hi=512),
+    # the 4-bit weight path (the page's -q4): same packs as the int8 one
+    "full_int4_packs2048": dict(cfg=EncoderConfig("full_int4_packs2048", precision="int4", seed=5, **FULL),
+                                n_packs=64, pack_budget=2048, len_lo=8, len_hi=512),
 }
+# A small config whose widths hold whole 256-input super-blocks (the 4-bit
+# format needs K % 256 == 0, which the tiny config's hidden 128 is not).
+SMALL_Q4 = dict(vocab=1000, hidden=256, heads=4, head_dim=64, intermediate=512, layers=3)
 WORKLOAD_ORDER = list(WORKLOADS)
 
 
@@ -136,6 +142,56 @@ def quantize_weight_blocks(w: np.ndarray, block: int = 32):
     return q.reshape(N, K), s
 
 
+def quantize_weight_q4(w: np.ndarray):
+    """Storage format of the 4-bit model, in the style of the Q4_K blocks the
+    page's -q4 repacks (asymmetric 4-bit codes, two-level scales):
+
+    per row, per 32 inputs (a block): codes q in [0, 15]; per 256 inputs (a
+    super-block of 8 blocks): fp32 d and dmin, and per block 6-bit indices
+    sc, mn in [0, 63].  The block's scale is es = fp32(d * sc), its offset
+    eo = fp32(dmin * mn), and the weight w = es * q - eo.
+
+    Construction: a block's range [min(lo, 0), hi] gives a = (hi - lo') / 15
+    and m = -lo'; d = max a / 63 and dmin = max m / 63 over the super-block;
+    sc = rint(a / d), mn = rint(m / dmin) (0 when d or dmin is 0); then
+    q = clamp(rint((w + eo) / es), 0, 15) (0 when es = 0).
+
+    Returns (codes uint8 [N, K/2], two per byte, the even input in the low
+    nibble; meta uint8 [N, K/128, 16]: per 128 inputs sc[4], mn[4] (one byte
+    each), then d and dmin of their super-block as fp32)."""
+    w = np.ascontiguousarray(w, dtype=np.float32)
+    N, K = w.shape
+    assert K % 256 == 0
+    nb = K // 32
+    wb = w.reshape(N, nb, 32)
+    lo = np.minimum(wb.min(axis=2), np.float32(0))
+    hi = wb.max(axis=2)
+    a = ((hi - lo) / np.float32(15)).astype(np.float32)
+    m = (-lo).astype(np.float32)
+    sa, sm = a.reshape(N, nb // 8, 8), m.reshape(N, nb // 8, 8)
+    d = (sa.max(axis=2) / np.float32(63)).astype(np.float32)
+    dmin = (sm.max(axis=2) / np.float32(63)).astype(np.float32)
+    sd = np.where(d > 0, d, np.float32(1))[:, :, None]
+    sdm = np.where(dmin > 0, dmin, np.float32(1))[:, :, None]
+    sc = np.where(d[:, :, None] > 0, np.clip(np.rint(sa / sd), 0, 63), 0).astype(np.uint8)
+    mn = np.where(dmin[:, :, None] > 0, np.clip(np.rint(sm / sdm), 0, 63), 0).astype(np.uint8)
+    es = (d[:, :, None] * sc.astype(np.float32)).astype(np.float32).reshape(N, nb)
+    eo = (dmin[:, :, None] * mn.astype(np.float32)).astype(np.float32).reshape(N, nb)
+    safe = np.where(es > 0, es, np.float32(1))[:, :, None]
+    q = np.where(es[:, :, None] > 0, np.clip(np.rint((wb + eo[:, :, None]) / safe), 0, 15), 0)
+    q = q.astype(np.uint8).reshape(N, K)
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    meta = np.zeros((N, K // 128, 16), np.uint8)
+    sc2, mn2 = sc.reshape(N, K // 128, 4), mn.reshape(N, K // 128, 4)
+    meta[:, :, 0:4] = sc2
+    meta[:, :, 4:8] = mn2
+    d2 = np.repeat(d, 2, axis=1)  # each super-block spans two 128-input groups
+    dm2 = np.repeat(dmin, 2, axis=1)
+    meta[:, :, 8:12] = d2.astype("<f4").view(np.uint8).reshape(N, K // 128, 4)
+    meta[:, :, 12:16] = dm2.astype("<f4").view(np.uint8).reshape(N, K // 128, 4)
+    return codes, meta
+
+
 def dequant_blocks(q: np.ndarray, s: np.ndarray, block: int = 32) -> np.ndarray:
     """fp64 values of a block-quantised matrix (exact: int8 times fp32 fits fp64)."""
     N, K = q.shape
@@ -147,8 +203,9 @@ def storage_weights(cfg: EncoderConfig, w32: Optional[dict] = None) -> dict:
 
     fp32: the fp32 arrays.  bf16: every matrix (embedding included) as uint16
     bf16 bits (key suffix _bf16).  int8: every matrix as (q int8, s fp32)
-    blocks of 32 along the input dimension (suffixes _q, _s).  LayerNorm gains
-    stay fp32 in every format.
+    blocks of 32 along the input dimension (suffixes _q, _s).  int4: the
+    layer matrices as quantize_weight_q4 (suffixes _q4, _q4m), the token
+    table as int8 blocks.  LayerNorm gains stay fp32 in every format.
     """
     if w32 is None:
         w32 = make_fp32_weights(cfg)
@@ -171,6 +228,16 @@ def storage_weights(cfg: EncoderConfig, w32: Optional[dict] = None) -> dict:
             d = {}
             for k in mats:
                 d[k + "_q"], d[k + "_s"] = quantize_weight_blocks(L[k])
+            d["attn_norm"], d["mlp_norm"] = L["attn_norm"], L["mlp_norm"]
+            out["layers"].append(d)
+    elif cfg.precision == "int4":
+        # the layer matrices in 4-bit blocks; the token table in the int8
+        # blocks (the page's Q4_K_M file keeps some tensors at more bits)
+        out["tok_emb_q"], out["tok_emb_s"] = quantize_weight_blocks(w32["tok_emb"])
+        for L in w32["layers"]:
+            d = {}
+            for k in mats:
+                d[k + "_q4"], d[k + "_q4m"] = quantize_weight_q4(L[k])
             d["attn_norm"], d["mlp_norm"] = L["attn_norm"], L["mlp_norm"]
             out["layers"].append(d)
     else:
@@ -209,8 +276,9 @@ def cached_storage_weights(cfg: EncoderConfig) -> dict:
 
 def _flat_names(cfg: EncoderConfig) -> List[str]:
     mats = ["wqkv", "wo", "wi", "wo2"]
-    suf = {"fp32": [""], "bf16": ["_bf16"], "int8": ["_q", "_s"]}[cfg.precision]
-    names = ["emb_norm", "final_norm"] + ["tok_emb" + s for s in suf]
+    suf = {"fp32": [""], "bf16": ["_bf16"], "int8": ["_q", "_s"], "int4": ["_q4", "_q4m"]}[cfg.precision]
+    emb_suf = ["_q", "_s"] if cfg.precision == "int4" else suf
+    names = ["emb_norm", "final_norm"] + ["tok_emb" + s for s in emb_suf]
     for l in range(cfg.layers):
         names += [f"l{l}_{m}{s}" for m in mats for s in suf]
         names += [f"l{l}_mlp_norm"] + ([f"l{l}_attn_norm"] if l > 0 else [])
