@@ -31,8 +31,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "encoded tokens/sec (25-layer 768-d encoder, ~2048-token packs) + % MFMA peak"
-PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3, "int8": 5000.0}
-DTYPE = {"bf16": "bf16", "fp32": "f32", "int8": "int8"}
+# the 4-bit path unpacks its codes to int8 and runs the int8 MFMA: int8 peak
+PEAK_TFLOPS = {"bf16": 2500.0, "fp32": 157.3, "int8": 5000.0, "int4": 5000.0}
+DTYPE = {"bf16": "bf16", "fp32": "f32", "int8": "int8", "int4": "int8 (4-bit weights)"}
 # flops per token of each GEMM class (H = 768, I = 3072): 2 * N * K
 GEMM_CLASSES = {"gemm_qkv": lambda H, I: 2 * 3 * H * H, "gemm_o": lambda H, I: 2 * H * H,
                 "gemm_geglu": lambda H, I: 2 * 2 * I * H, "gemm_o2": lambda H, I: 2 * H * I}
@@ -81,7 +82,7 @@ def class_work(cfg, packs):
         g, loc = allowed_pairs(np.diff(p.offsets), cfg.window)
         pg, pl = pg + g, pl + loc
     per_pair = 4 * cfg.head_dim * cfg.heads
-    out_b = {"bf16": 2, "fp32": 4, "int8": 1}[cfg.precision]
+    out_b = {"bf16": 2, "fp32": 4, "int8": 1, "int4": 1}[cfg.precision]
     w = {k: (f(H, I) * T * Lyr, "TFLOP/s", gemm_peak) for k, f in GEMM_CLASSES.items()}
     w["attn_global"] = (pg * per_pair * n_glob, "TFLOP/s", attn_peak)
     w["attn_local"] = (pl * per_pair * (Lyr - n_glob), "TFLOP/s", attn_peak)

@@ -50,10 +50,20 @@ typedef enum {
   TTE_FP32 = 0, /* fp32 weights and activations, fp32 matrix cores */
   TTE_BF16 = 1, /* bf16 weights and matmul/attention operands, fp32 accumulate,
                    fp32 residual stream, norms and softmax statistics */
-  TTE_INT8 = 2  /* int8 weight blocks of 32 inputs with fp32 scales; every
+  TTE_INT8 = 2, /* int8 weight blocks of 32 inputs with fp32 scales; every
                    weight matmul input rounded per row to 7 bits (|q| <= 63)
                    with an fp32 row scale; int8 matrix cores, int32 sums per
                    block; attention, norms and residual in fp32 */
+  TTE_INT4 = 3  /* the page's -q4 (section 精度と量子化): layer matrices as
+                   asymmetric 4-bit blocks of 32 inputs (codes 0..15, two per
+                   byte, the even input in the low nibble), with per 128
+                   inputs a 16-byte record: four 6-bit block scales sc and
+                   offsets mn (a byte each), then the fp32 d and dmin of
+                   their 256-input super-block; block scale es = fp32(d*sc),
+                   offset eo = fp32(dmin*mn), weight es*q - eo.  The token
+                   table is int8 blocks as in TTE_INT8.  Activations, MFMA
+                   and the rest as TTE_INT8; hidden and intermediate must be
+                   multiples of 256 */
 } tte_precision;
 
 /* Execution options (tte_config.flags). */
@@ -90,7 +100,9 @@ typedef struct {
 
 /* Device pointers to one layer's weights, in the storage format of the
  * precision: fp32 or bf16 (raw uint16 bits) arrays, or int8 codes with fp32
- * scales [out, in/32] (the *_scale pointers are read only in TTE_INT8). */
+ * scales [out, in/32] (the *_scale pointers are read only in TTE_INT8); in
+ * TTE_INT4 each matrix is codes [out, in/2] bytes and its *_scale pointer
+ * the records [out, in/128] x 16 bytes. */
 typedef struct {
   const void* wqkv;  const float* wqkv_scale;  /* [3H, H]: rows Q, then K, then V; head j at rows j*64.. */
   const void* wo;    const float* wo_scale;    /* [H, H] */

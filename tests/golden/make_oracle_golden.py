@@ -29,6 +29,7 @@ SELECTION = {
     "full_bf16_packs2048": [(0, None), (1, None)],
     "full_bf16_4x4096": [(0, [0])],
     "full_int8_packs2048": [(0, None), (1, None)],
+    "full_int4_packs2048": [(0, None)],
 }
 
 

@@ -26,14 +26,15 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 # end-to-end int8 gate is min cos >= 0.998 and mean cos >= 0.999; the integer
 # product itself is checked bit-exact at the GEMM level, and the first layers
 # of the full model are checked tightly before flips accumulate.
-COS_GATE = {"fp32": 0.99999, "bf16": 0.999, "int8": 0.998}
+# The 4-bit path takes the same 7-bit activation codes, so the same gate.
+COS_GATE = {"fp32": 0.99999, "bf16": 0.999, "int8": 0.998, "int4": 0.998}
 
 
 def _gate(got, ref, precision):
     cos = row_cosines(got, ref)
     assert np.all(np.abs(np.linalg.norm(got, axis=1) - 1) < 1e-5), np.linalg.norm(got, axis=1)
     assert cos.min() >= COS_GATE[precision], cos
-    if precision == "int8":
+    if precision in ("int8", "int4"):
         assert cos.mean() >= 0.999, cos
     if precision == "fp32":
         assert np.abs(got - ref).max() <= 1e-4, np.abs(got - ref).max()
@@ -136,6 +137,47 @@ def test_packed_equals_alone_and_deterministic(tiny_models, precision):
     _gate(a, ref, precision)
 
 
+@pytest.fixture(scope="module")
+def small_q4_model():
+    """The 4-bit format needs widths of whole 256-input super-blocks, which
+    the tiny config's hidden 128 is not: a 3-layer hidden-256 model."""
+    cfg = ti.EncoderConfig("small_q4", precision="int4", seed=6, **ti.SMALL_Q4)
+    w = ti.storage_weights(cfg)
+    m = Model(cfg, w, max_tokens=2048, max_text_len=1024, max_texts=64)
+    yield cfg, w, m
+    m.close()
+
+
+def test_small_int4_pack_matches_oracle(small_q4_model):
+    cfg, w, m = small_q4_model
+    pack = ti.random_pack(np.random.default_rng(41), [8, 40, 130, 1, 65, 300, 2], cfg.vocab)
+    say(f"small int4: T={pack.n_tokens}")
+    ids = dev(pack.ids)
+    got = host(m.embed_pack(ids, pack.offsets))
+    assert np.array_equal(got, host(m.embed_pack(ids, pack.offsets))), "two runs differ"
+    ref = oracle.encode(cfg.as_dict(), w, pack.ids, pack.offsets)
+    cos = _gate(got, ref, "int4")
+    say(f"  cos min {cos.min():.8f} mean {cos.mean():.8f}")
+    for i in (0, 3, 5):
+        t = pack.text(i)
+        alone = host(m.embed_pack(dev(t), np.array([0, len(t)], np.int32)))
+        np.testing.assert_allclose(alone[0], got[i], atol=2e-3)
+
+
+def test_small_int4_layer_trace_matches_oracle(small_q4_model):
+    """Per-token residual states of the 4-bit model after every layer: the
+    first states are checked before activation-code flips accumulate."""
+    cfg, w, m = small_q4_model
+    pack = ti.random_pack(np.random.default_rng(43), [8, 40, 130], cfg.vocab)
+    states, _ = m.trace(dev(pack.ids), pack.offsets, cfg.layers)
+    got = host(states)
+    ref = oracle.encode_layers(cfg.as_dict(), w, pack.ids, pack.offsets)
+    for l, r in enumerate(ref):
+        cos = row_cosines(got[l], r)
+        say(f"  state {l}: token cos min {cos.min():.8f}")
+        assert cos.min() >= (1 - 1e-4 if l <= 1 else 0.998), (l, cos.min())
+
+
 def test_edge_cases(tiny_models):
     cfg, w, m = tiny_models["fp32"]
     t = torch()
@@ -201,7 +243,8 @@ def _golden(name, pack_index):
 # of the ~2k-token packs (the 16k-token packs stay unsplit)
 FULL_CASES = [("full_fp32_957", 0, False), ("full_bf16_packs2048", 0, False), ("full_bf16_packs2048", 1, False),
               ("full_int8_packs2048", 0, False), ("full_int8_packs2048", 1, False), ("full_bf16_4x4096", 0, False),
-              ("full_fp32_957", 0, True), ("full_bf16_packs2048", 1, True), ("full_int8_packs2048", 0, True)]
+              ("full_fp32_957", 0, True), ("full_bf16_packs2048", 1, True), ("full_int8_packs2048", 0, True),
+              ("full_int4_packs2048", 0, False), ("full_int4_packs2048", 0, True)]
 
 
 @pytest.fixture(scope="module")
@@ -241,7 +284,8 @@ def test_full_size_matches_oracle(full_models, name, pack_index, split_k):
 
 
 @pytest.mark.parametrize("name,split_k", [("full_fp32_957", False), ("full_bf16_packs2048", False),
-                                          ("full_bf16_packs2048", True), ("full_int8_packs2048", False)])
+                                          ("full_bf16_packs2048", True), ("full_int8_packs2048", False),
+                                          ("full_int4_packs2048", False)])
 def test_full_size_per_token_output_pools_to_embeddings(full_models, name, split_k):
     """At full size: mean pooling + L2 of tte_embed_tokens's output equals
     tte_embed's vectors (the same pass up to the final norm), and every
@@ -261,7 +305,8 @@ def test_full_size_per_token_output_pools_to_embeddings(full_models, name, split
 
 
 @pytest.mark.parametrize("name,split_k", [("full_fp32_957", False), ("full_bf16_packs2048", False),
-                                          ("full_int8_packs2048", False), ("full_fp32_957", True),
+                                          ("full_int8_packs2048", False), ("full_int4_packs2048", False),
+                                          ("full_fp32_957", True),
                                           ("full_bf16_packs2048", True)])
 def test_full_size_first_layers_trace(full_models, name, split_k):
     """Residual stream after the embedding norm and the first two layers
@@ -278,5 +323,5 @@ def test_full_size_first_layers_trace(full_models, name, split_k):
         cos = row_cosines(got[l], r)
         rel = np.abs(got[l] - r).max() / np.abs(r).max()
         say(f"  {name} state {l}: token cos min {cos.min():.8f} max rel {rel:.2e}")
-        gate = {"fp32": 1 - 1e-9, "bf16": 1 - 1e-4, "int8": 1 - 1e-4}[cfg.precision]
+        gate = {"fp32": 1 - 1e-9, "bf16": 1 - 1e-4, "int8": 1 - 1e-4, "int4": 1 - 1e-4}[cfg.precision]
         assert cos.min() >= gate, (l, cos.min())

@@ -210,6 +210,110 @@ def test_gemm_int8_scaled(M, N, K):
         np.testing.assert_allclose(host(cg), oracle.geglu(ref), atol=4e-6 * scale * scale + 1e-6, rtol=1e-4)
 
 
+# 4-bit weights: K a multiple of 256; 4-wave 32/64-row tiles and 128x128
+# (>= 1024 tiles), 2 and 3 stages
+Q4_SHAPES = [(178, 384, 256), (957, 2304, 768), (300, 768, 3072), (130, 512, 256), (1, 128, 256),
+             (4100, 4096, 256), (1913, 2304, 768), (8200, 768, 3072)]
+
+
+def _q4_pack(q, sc, mn, d, dmin):
+    """Packed codes and per-128 records from codes q [N, K] in [0, 15],
+    per-32 sc, mn [N, K/32] and per-128 fp32 d, dmin [N, K/128]."""
+    N, K = q.shape
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    meta = np.zeros((N, K // 128, 16), np.uint8)
+    meta[:, :, 0:4] = sc.reshape(N, K // 128, 4)
+    meta[:, :, 4:8] = mn.reshape(N, K // 128, 4)
+    meta[:, :, 8:12] = np.asarray(d, "<f4").view(np.uint8).reshape(N, K // 128, 4)
+    meta[:, :, 12:16] = np.asarray(dmin, "<f4").view(np.uint8).reshape(N, K // 128, 4)
+    return codes, meta
+
+
+def _q4_exact_operands(M, N, K, rng):
+    """Operands whose product every fp32 step represents exactly: codes and
+    indices small integers, d and dmin powers of two >= 1/4, and
+    sum |terms| < 2^22 in units of 1/4."""
+    amax = 63 if K <= 1024 else 15
+    qx = rng.integers(-amax, amax + 1, size=(M, K)).astype(np.int8)
+    q = rng.integers(0, 16, size=(N, K)).astype(np.uint8)
+    sc = rng.integers(1, 4, size=(N, K // 32)).astype(np.uint8)
+    mn = rng.integers(0, 9, size=(N, K // 32)).astype(np.uint8)
+    d = rng.choice(np.array([0.25, 0.5, 1.0], np.float32), size=(N, K // 128))
+    dmin = rng.choice(np.array([0.5, 1.0], np.float32), size=(N, K // 128))
+    codes, meta = _q4_pack(q, sc, mn, d, dmin)
+    bound = (K // 32) * 32 * amax * (3 * 15 + 8) * 4
+    assert bound < 2 ** 24
+    return qx, codes, meta
+
+
+@pytest.mark.parametrize("M,N,K", Q4_SHAPES)
+def test_gemm_int4_exact(M, N, K):
+    """Every block scale, offset and partial sum representable: the output
+    equals the fp64 definition exactly, so a wrong nibble order, record
+    field or block index shows as a mismatch, not as a small error."""
+    t = torch()
+    say(f"gemm int4 exact {M}x{N}x{K}")
+    rng = np.random.default_rng(19 * M + N + K)
+    qx, codes, meta = _q4_exact_operands(M, N, K, rng)
+    sx = np.ones(M, np.float32)
+    exact = oracle.block_matmul_q4(qx, sx, codes, meta)
+    dqx, dsx, dqw, dsw = dev(qx), dev(sx), dev(codes), dev(meta)
+    c = empty((M, N), t.float32)
+    _run_gemm(B.TTE_INT4, B.TTE_EPI_STORE, dqx, dsx, dqw, dsw, M, N, K, c, B.TTE_OUT_F32)
+    got = host(c)
+    bad = np.argwhere(got != exact)
+    assert bad.size == 0, (bad[:5], got[tuple(bad[0])], exact[tuple(bad[0])])
+
+
+def _q4_bound(qx, sx, codes, meta):
+    """A bound on the fp32 evaluation error of block_matmul_q4: every partial
+    sum is at most sx * sum |qx| (|es q| + |eo|) in magnitude, and each of
+    the 2 K/32 + 2 fused steps rounds once."""
+    q = oracle.q4_codes(codes)
+    N, K = q.shape
+    es, eo = oracle.q4_block_params(meta)
+    mag = (np.abs(q.astype(np.float64)).reshape(N, K // 32, 32) * es.astype(np.float64)[:, :, None]
+           + eo.astype(np.float64)[:, :, None]).reshape(N, K)
+    total = np.abs(np.asarray(sx, np.float64))[:, None] * (np.abs(qx.astype(np.float64)) @ mag.T)
+    return (2 * K // 32 + 2) * 2.0 ** -24 * total
+
+
+@pytest.mark.parametrize("M,N,K", Q4_SHAPES)
+def test_gemm_int4_scaled(M, N, K):
+    """Quantised weights and 7-bit activations against the oracle's
+    block_matmul_q4, in the store, residual and GeGLU epilogues."""
+    t = torch()
+    say(f"gemm int4 scaled {M}x{N}x{K}")
+    rng = np.random.default_rng(23 * M + N + K)
+    x = rng.normal(size=(M, K)).astype(np.float32)
+    x[0] = 0.0  # a zero row: scale 0
+    qx, sx = oracle.quantize_rows_7bit(x)
+    codes, meta = ti.quantize_weight_q4(rng.normal(0, 0.02, size=(N, K)).astype(np.float32))
+    meta[0, 0, :] = 0  # a zero record: es = eo = 0 for its 128 inputs
+    ref = oracle.block_matmul_q4(qx, sx, codes, meta)
+    tol = _q4_bound(qx, sx, codes, meta) + 1e-30
+    dqx, dsx, dqw, dsw = dev(qx), dev(sx), dev(codes), dev(meta)
+    c = empty((M, N), t.float32)
+    _run_gemm(B.TTE_INT4, B.TTE_EPI_STORE, dqx, dsx, dqw, dsw, M, N, K, c, B.TTE_OUT_F32)
+    got = host(c)
+    assert np.all(np.abs(got - ref) <= tol), np.abs(got - ref).max()
+    assert np.all(got[0] == 0)
+    r = rng.normal(size=(M, N)).astype(np.float32)
+    cr = dev(r)
+    _run_gemm(B.TTE_INT4, B.TTE_EPI_RESIDUAL, dqx, dsx, dqw, dsw, M, N, K, cr, B.TTE_OUT_F32)
+    assert np.all(np.abs(host(cr) - (r + ref)) <= tol + 2.0 ** -23 * np.abs(r + ref))
+    if N % 128 == 0:
+        half = N // 2
+        cg = empty((M, half), t.float32)
+        _run_gemm(B.TTE_INT4, B.TTE_EPI_GEGLU, dqx, dsx, dqw, dsw, M, half, K, cg, B.TTE_OUT_F32)
+        scale = np.abs(ref).max()
+        np.testing.assert_allclose(host(cg), oracle.geglu(ref), atol=1e-5 * scale * scale + 1e-6, rtol=1e-4)
+        cb = empty((M, half), t.int16)
+        _run_gemm(B.TTE_INT4, B.TTE_EPI_GEGLU, dqx, dsx, dqw, dsw, M, half, K, cb, B.TTE_OUT_BF16)
+        got_b = ti.bf16_to_f32(host(cb).view(np.uint16)).astype(np.float64)
+        np.testing.assert_allclose(got_b, oracle.geglu(ref), atol=1e-5 * scale * scale + 1e-6, rtol=2.0 ** -8)
+
+
 # split-K residual projection: (M, N, K, splits); 2 or 3 stages per part
 SPLIT_SHAPES = [(957, 768, 3072, 2), (1913, 768, 3072, 4), (178, 384, 256, 2), (65, 256, 1536, 3), (1, 128, 512, 2)]
 
@@ -222,6 +326,13 @@ def _split_operands(prec, M, N, K, rng):
         qw, sw = ti.quantize_weight_blocks(rng.normal(0, 0.02, size=(N, K)).astype(np.float32))
         return (B.TTE_INT8, dev(qx), dev(sx), dev(qw), dev(sw),
                 lambda k0, k1: oracle.block_matmul_int8(qx[:, k0:k1], sx, qw[:, k0:k1], sw[:, k0 // 32:k1 // 32]))
+    if prec == "int4":
+        x = rng.normal(size=(M, K)).astype(np.float32)
+        qx, sx = oracle.quantize_rows_7bit(x)
+        codes, meta = ti.quantize_weight_q4(rng.normal(0, 0.02, size=(N, K)).astype(np.float32))
+        return (B.TTE_INT4, dev(qx), dev(sx), dev(codes), dev(meta),
+                lambda k0, k1: oracle.block_matmul_q4(qx[:, k0:k1], sx, codes[:, k0 // 2:k1 // 2],
+                                                      meta[:, k0 // 128:k1 // 128]))
     a = rng.normal(size=(M, K)).astype(np.float32)
     w = rng.normal(0, 0.02, size=(N, K)).astype(np.float32)
     if prec == "bf16":
@@ -233,7 +344,7 @@ def _split_operands(prec, M, N, K, rng):
 
 
 @pytest.mark.parametrize("M,N,K,splits", SPLIT_SHAPES)
-@pytest.mark.parametrize("prec", ["fp32", "bf16", "int8"])
+@pytest.mark.parametrize("prec", ["fp32", "bf16", "int8", "int4"])
 def test_gemm_splitk_partials(M, N, K, splits, prec):
     t = torch()
     say(f"gemm split-K {prec} {M}x{N}x{K} / {splits}")
@@ -408,7 +519,7 @@ def test_pool(lengths):
 # QKV projection with the fused RoPE / transposed-V epilogue
 # --------------------------------------------------------------------------
 
-@pytest.mark.parametrize("precision", ["fp32", "bf16", "int8"])
+@pytest.mark.parametrize("precision", ["fp32", "bf16", "int8", "int4"])
 # 178 and 433 tokens take the 128-row tiles, 1913 the 192-row ones (bf16)
 @pytest.mark.parametrize("lengths", [[8, 40, 130], [1, 64, 65, 300, 3], [500, 700, 713]])
 @pytest.mark.parametrize("layer", [0, 1])
@@ -429,6 +540,10 @@ def test_qkv_rope_epilogue(precision, lengths, layer):
         qx, sx = oracle.quantize_rows_7bit(x)
         da, ds = dev(qx), dev(sx)
         raw = oracle.block_matmul_int8(qx, sx, L["wqkv_q"], L["wqkv_s"])
+    elif precision == "int4":
+        qx, sx = oracle.quantize_rows_7bit(x)
+        da, ds = dev(qx), dev(sx)
+        raw = oracle.block_matmul_q4(qx, sx, L["wqkv_q4"], L["wqkv_q4m"])
     elif precision == "bf16":
         xb = ti.bf16_bits(x)
         da, ds = dev(xb), None

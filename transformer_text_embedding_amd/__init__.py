@@ -89,6 +89,8 @@ class Model:
             return self._dev(d[name]), None
         if self.precision == "bf16":
             return self._dev(d[name + "_bf16"]), None
+        if self.precision == "int4" and name != "tok_emb":
+            return self._dev(d[name + "_q4"]), self._dev(d[name + "_q4m"])
         return self._dev(d[name + "_q"]), self._dev(d[name + "_s"])
 
     def _upload(self, w: dict):

@@ -15,9 +15,9 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "tte.h")
 
 TTE_OK, TTE_E_INVALID, TTE_E_UNSUPPORTED, TTE_E_NOMEM, TTE_E_DEVICE = range(5)
 STATUS_NAMES = {0: "TTE_OK", 1: "TTE_E_INVALID", 2: "TTE_E_UNSUPPORTED", 3: "TTE_E_NOMEM", 4: "TTE_E_DEVICE"}
-TTE_FP32, TTE_BF16, TTE_INT8 = 0, 1, 2
+TTE_FP32, TTE_BF16, TTE_INT8, TTE_INT4 = 0, 1, 2, 3
 TTE_FLAG_SPLIT_K = 1
-PRECISIONS = {"fp32": TTE_FP32, "bf16": TTE_BF16, "int8": TTE_INT8}
+PRECISIONS = {"fp32": TTE_FP32, "bf16": TTE_BF16, "int8": TTE_INT8, "int4": TTE_INT4}
 TTE_OUT_F32, TTE_OUT_BF16, TTE_OUT_I8 = 0, 1, 2
 TTE_EPI_STORE, TTE_EPI_RESIDUAL, TTE_EPI_GEGLU = 0, 1, 2
 KERNEL_CLASSES = ["embed", "norm", "quant", "gemm_qkv", "attn_global", "attn_local", "gemm_o", "gemm_geglu",

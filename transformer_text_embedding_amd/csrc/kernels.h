@@ -8,7 +8,10 @@
 
 namespace tte {
 
-enum Prec { P_F32 = 0, P_BF16 = 1, P_I8 = 2 };
+// P_I4: 4-bit weight codes (two per byte) with a 16-byte record per 128
+// inputs of a weight row (block scales and offsets), 7-bit int8 activation
+// codes; numbered as the ABI's precisions.
+enum Prec { P_F32 = 0, P_BF16 = 1, P_I8 = 2, P_I4 = 3 };
 enum OutKind { O_F32 = 0, O_BF16 = 1, O_I8 = 2 };
 enum Epi { E_STORE = 0, E_RESID = 1, E_GEGLU = 2, E_QKV = 3, E_PART = 4 };
 

@@ -34,6 +34,12 @@
 //         block), then acc += float(sum) * w_scale[n, block] in fp32; the
 //         block scales of the W tile ride the same LDS ring; the row scale
 //         a_scale[m] multiplies once in the epilogue.
+//   int4 (weights; activations int8): W rows are 64 bytes of packed codes
+//         per 128-input K tile and unpack to int8 in registers before the
+//         same MFMA; a second MFMA against all-ones gives the activations'
+//         block sum S, and acc += float(P) * es - float(S) * eo with the
+//         block's scale and offset decoded from the 16-byte record that
+//         rides the LDS ring where the int8 scales do.
 //
 // Epilogues: STORE (fp32 or bf16), RESID (fp32 C += result), GEGLU.  For
 // GEGLU the W tile rows are chosen so that the first half of every wave's
@@ -53,7 +59,7 @@ namespace {
 
 template <int PREC>
 struct Fmt {
-  static constexpr int ES = PREC == P_F32 ? 4 : (PREC == P_BF16 ? 2 : 1);
+  static constexpr int ES = PREC == P_F32 ? 4 : (PREC == P_BF16 ? 2 : 1);  // A element bytes
 };
 
 // Block of WGM x WGN waves; each wave owns WM x WN MFMA 16x16 output tiles.
@@ -69,17 +75,24 @@ struct Cfg {
   static constexpr int BM = 16 * WM * WGM;
   static constexpr int BN = 16 * WN * WGN;
   static constexpr int ROWS = BM + BN;
-  static constexpr int SCALE_BYTES = PREC == P_I8 ? BN * 16 : 0;  // int8: fp32 scales of 4 blocks per W row
-  static constexpr int TILE = ROWS * KT + SCALE_BYTES;
+  static constexpr bool Q4 = PREC == P_I4;
+  static constexpr int WROW = Q4 ? KT / 2 : KT;  // bytes of a W row per K tile (int4: packed codes)
+  static constexpr int AREG = BM * KT;           // LDS bytes of the A rows, then the W rows
+  static constexpr int WREG = BN * WROW;
+  // int8: fp32 scales of 4 blocks per W row; int4: the 16-byte record
+  static constexpr int SCALE_BYTES = (PREC == P_I8 || Q4) ? BN * 16 : 0;
+  static constexpr int TILE = AREG + WREG + SCALE_BYTES;
   static constexpr int STAGES = STAGES_;
   static constexpr int LDS = STAGES * TILE;
-  static constexpr int Q = ROWS * KT / 1024;  // 1 KB load instructions per K tile
-  static constexpr int QW = Q / NW;           // per wave
-  static constexpr int PER_TILE = QW + (PREC == P_I8 ? 1 : 0);  // vector-memory ops per wave per tile
-  static_assert(ROWS * KT % 1024 == 0 && Q % NW == 0, "tile rows must split evenly over the waves");
-  static_assert(QW * NW * 1024 == ROWS * KT, "the load instructions cover the tile exactly");
-  static_assert(PREC != P_I8 || BN == 32 * NW, "int8 scale staging: 32 W rows per wave");
-  static_assert(KT == 128 || ((KT == 64 || KT == 256) && PREC != P_I8), "K tile of 128 bytes, or 64 / 256 for fp32 / bf16");
+  static constexpr int QA = AREG / 1024;           // 1 KB load instructions of the A rows
+  static constexpr int Q = (AREG + WREG) / 1024;   // 1 KB load instructions per K tile
+  static constexpr int QW = Q / NW;                // per wave
+  static constexpr int PER_TILE = QW + ((PREC == P_I8 || Q4) ? 1 : 0);  // vector-memory ops per wave per tile
+  static_assert(AREG % 1024 == 0 && WREG % 1024 == 0 && Q % NW == 0, "tile rows must split evenly over the waves");
+  static_assert(QW * NW * 1024 == AREG + WREG, "the load instructions cover the tile exactly");
+  static_assert((PREC != P_I8 && !Q4) || BN == 32 * NW, "int8 / int4 scale staging: 32 W rows per wave");
+  static_assert(KT == 128 || ((KT == 64 || KT == 256) && PREC != P_I8 && !Q4),
+                "K tile of 128 bytes, or 64 / 256 for fp32 / bf16");
   static_assert(LDS <= 160 * 1024, "LDS budget");
 };
 
@@ -102,13 +115,24 @@ __device__ __forceinline__ int w_row(int r, int nb, int N) {
 // instructions of A/W rows, and for int8 the 16-byte scale vectors of 32 W
 // rows (lanes 0..31 of every wave).
 template <int QW, int PREC, int KT>
-__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* const* src, const float* s_src, int kt,
-                                           int wid, int lane, int rows) {
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* const* src, const int* step,
+                                           const float* s_src, int kt, int wid, int lane, int scale_at) {
 #pragma unroll
-  for (int j = 0; j < QW; ++j) dma16(src[j] + (size_t)kt * KT, stage + (wid * QW + j) * 1024);
-  if constexpr (PREC == P_I8) {
-    if (lane < 32) dma16(s_src + kt * 4, stage + rows * KT + wid * 512);
+  for (int j = 0; j < QW; ++j) dma16(src[j] + (size_t)kt * step[j], stage + (wid * QW + j) * 1024);
+  if constexpr (PREC == P_I8 || PREC == P_I4) {
+    if (lane < 32) dma16(s_src + kt * 4, stage + scale_at + wid * 512);
   }
+}
+
+// 8 packed 4-bit codes (4 bytes, the even input in the low nibble) as 8
+// int8 values in input order.
+__device__ __forceinline__ long unpack_q4(uint32_t x) {
+  const uint32_t lo = x & 0x0F0F0F0Fu, hi = (x >> 4) & 0x0F0F0F0Fu;  // codes 0, 2, 4, 6 / 1, 3, 5, 7
+  // v_perm_b32: bytes 0..3 of the second operand are selectors 0..3, of the
+  // first 4..7
+  const uint32_t a = __builtin_amdgcn_perm(hi, lo, 0x05010400u);  // codes 0, 1, 2, 3
+  const uint32_t b = __builtin_amdgcn_perm(hi, lo, 0x07030602u);  // codes 4, 5, 6, 7
+  return (long)(((uint64_t)b << 32) | a);
 }
 
 template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES, int WGM, int WGN, int KT>
@@ -150,7 +174,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
   // consecutive rows, one chunk) spread over distinct bank groups:
   //   KT = 256 (16 chunks): swizzle(r) = r & 15;
   //   KT = 128 (8 chunks):  swizzle(r) = r & 7;
-  //   KT = 64 (4 chunks):   swizzle(r) = ((r >> 1) ^ (r >> 3)) & 3, which
+  //   KT = 64 (4 chunks):   swizzle(r) = ((i >> 1) ^ (i >> 3)) & 3 with
+  //   i = r & 15 (the fragment reads know a row only modulo 16), which
   //   puts any 8 consecutive rows in 8 distinct slots of a 128-byte window
   //   and 16 consecutive rows in 16 distinct slots of 256 bytes.
   // Load plan: instruction j of this wave fills the 1 KB of LDS rows
@@ -158,20 +183,33 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
   // (KT/16), slot lane % (KT/16), which holds chunk slot ^ swizzle(row).
   constexpr int CPRW = KT / 16, RPI = 1024 / KT;  // chunks per row, rows per load instruction
   const int lrow = lane / CPRW, slot = lane % CPRW;
+  // int4: the W rows are KT/2 bytes (packed codes) and take the 64-byte
+  // row plan (16 rows per instruction, 4-chunk swizzle) after the A rows.
   const uint8_t* src[G::QW];
+  int step[G::QW];  // bytes a row advances per K tile
 #pragma unroll
   for (int j = 0; j < G::QW; ++j) {
-    const int r = RPI * (wid * G::QW + j) + lrow;
-    const int chunk = slot ^ (KT == 256 ? (r & 15) : KT == 128 ? (r & 7) : (((r >> 1) ^ (r >> 3)) & 3));
+    const int q = wid * G::QW + j;
+    if (G::Q4 && q >= G::QA) {
+      const int r = 16 * (q - G::QA) + (lane >> 2);  // W row of the tile
+      const int i = lane >> 2;  // r & 15
+      const int chunk = (lane & 3) ^ (((i >> 1) ^ (i >> 3)) & 3);
+      src[j] = W + (size_t)w_row<EPI, BN, WGN>(r, nb, N) * (K / 2) + (size_t)split * (k_part / 2) + chunk * 16;
+      step[j] = KT / 2;
+      continue;
+    }
+    const int r = RPI * q + lrow;
+    const int chunk = slot ^ (KT == 256 ? (r & 15) : KT == 128 ? (r & 7) : ((((r & 15) >> 1) ^ ((r & 15) >> 3)) & 3));
     if (r < BM)
       src[j] = A + (size_t)min(m0 + r, M - 1) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
     else
       src[j] = W + (size_t)w_row<EPI, BN, WGN>(r - BM, nb, N) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
+    step[j] = KT;
   }
-  // int8: lanes 0..31 of wave w load the 4 block scales (16 bytes) of W row
-  // 32 w + lane of the tile.
+  // int8 / int4: lanes 0..31 of wave w load the 16 bytes (int8: 4 block
+  // scales; int4: the record) of W row 32 w + lane of the tile per K tile.
   const float* s_src = nullptr;
-  if constexpr (PREC == P_I8)
+  if constexpr (PREC == P_I8 || PREC == P_I4)
     s_src = w_scale + (size_t)w_row<EPI, BN, WGN>(wid * 32 + (lane & 31), nb, N) * (K / 32) + split * (k_part / 32);
 
   f32x4 acc[WM][WN];
@@ -181,7 +219,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
     for (int b = 0; b < WN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int p = 0; p < G::STAGES - 1 && p < nk; ++p)
-    issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, src, s_src, p, wid, lane, G::ROWS);
+    issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, src, step, s_src, p, wid, lane, G::AREG + G::WREG);
 
   const int swz = KT == 256 ? li : KT == 128 ? (li & 7) : (((li >> 1) ^ (li >> 3)) & 3);
   for (int kt = 0; kt < nk; ++kt) {
@@ -192,12 +230,12 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
     __builtin_amdgcn_s_barrier();
     // the stage of tile kt - 1 is free: every wave finished reading it
     if (kt + G::STAGES - 1 < nk)
-      issue_tile<G::QW, PREC, KT>(smem + ((kt + G::STAGES - 1) % G::STAGES) * G::TILE, src, s_src, kt + G::STAGES - 1,
-                              wid, lane, G::ROWS);
+      issue_tile<G::QW, PREC, KT>(smem + ((kt + G::STAGES - 1) % G::STAGES) * G::TILE, src, step, s_src,
+                                  kt + G::STAGES - 1, wid, lane, G::AREG + G::WREG);
 
     const uint8_t* stage = smem + (kt % G::STAGES) * G::TILE;
     const uint8_t* As = stage + (wm * 16 * WM + li) * ROW;
-    const uint8_t* Bs = stage + (BM + wn * 16 * WN + li) * ROW;
+    const uint8_t* Bs = stage + G::AREG + (wn * 16 * WN + li) * G::WROW;
 
     if constexpr (PREC == P_F32 || PREC == P_BF16) {
 #pragma unroll
@@ -229,8 +267,41 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
               acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[mt], bf[nt], acc[mt][nt], 0, 0, 0);
         }
       }
+    } else if constexpr (PREC == P_I4) {
+      // record of this lane's W row: sc[4], mn[4] (bytes), d, dmin (fp32)
+      const uint8_t* rec = stage + G::AREG + G::WREG + 16 * (wn * 16 * WN + li);
+      u32x4 rw[WN];
+#pragma unroll
+      for (int nt = 0; nt < WN; ++nt) rw[nt] = *reinterpret_cast<const u32x4*>(rec + 16 * 16 * nt);
+      const int swz4 = ((li >> 1) ^ (li >> 3)) & 3;  // the W rows' 64-byte swizzle (row & 15 = li)
+      const long ones = 0x0101010101010101l;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int off = (((2 * c + (g >> 1)) ^ swz) << 4) + ((g & 1) << 3);
+        long af[WM], bf[WN];
+#pragma unroll
+        for (int t = 0; t < WM; ++t) af[t] = *reinterpret_cast<const long*>(As + t * 16 * ROW + off);
+#pragma unroll
+        for (int t = 0; t < WN; ++t)
+          bf[t] = unpack_q4(*reinterpret_cast<const uint32_t*>(Bs + t * 16 * G::WROW + ((c ^ swz4) << 4) + 4 * g));
+#pragma unroll
+        for (int mt = 0; mt < WM; ++mt) {
+          // S: the activations' block sum, the same in every column
+          const i32x4 sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[mt], ones, i32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+          for (int nt = 0; nt < WN; ++nt) {
+            const float d = __uint_as_float(rw[nt][2]), dmin = __uint_as_float(rw[nt][3]);
+            const float es = d * (float)((rw[nt][0] >> (8 * c)) & 0xFF);
+            const float eo = dmin * (float)((rw[nt][1] >> (8 * c)) & 0xFF);
+            const i32x4 p = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[mt], bf[nt], i32x4{0, 0, 0, 0}, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+              acc[mt][nt][r] = __builtin_fmaf(-(float)sum[r], eo, __builtin_fmaf((float)p[r], es, acc[mt][nt][r]));
+          }
+        }
+      }
     } else {
-      const float* sc = reinterpret_cast<const float*>(stage + G::ROWS * ROW);
+      const float* sc = reinterpret_cast<const float*>(stage + G::AREG + G::WREG);
       f32x4 sw[WN];
 #pragma unroll
       for (int nt = 0; nt < WN; ++nt) sw[nt] = *reinterpret_cast<const f32x4*>(sc + 4 * (wn * 16 * WN + nt * 16 + li));
@@ -272,7 +343,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
       for (int mt = 0; mt < WM; ++mt) {
         const int m_slab = m0 + wm * 16 * WM + mt * 16;
         float rs[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (PREC == P_I8) {
+        if constexpr (PREC == P_I8 || PREC == P_I4) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) rs[r] = a_scale[min(m_slab + 4 * g + r, M - 1)];
         }
@@ -319,7 +390,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
       for (int mt = 0; mt < WM; ++mt) {
         const int mr = m0 + wm * 16 * WM + mt * 16 + 4 * g;
         float rs[4] = {1.f, 1.f, 1.f, 1.f};
-        if constexpr (PREC == P_I8) {
+        if constexpr (PREC == P_I8 || PREC == P_I4) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) rs[r] = mr + r < M ? a_scale[mr + r] : 0.f;
         }
@@ -371,7 +442,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
   for (int mt = 0; mt < WM; ++mt) {
     const int m_slab = m0 + wm * 16 * WM + mt * 16;
     float rs[4] = {1.f, 1.f, 1.f, 1.f};
-    if constexpr (PREC == P_I8) {
+    if constexpr (PREC == P_I8 || PREC == P_I4) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) rs[r] = a_scale[min(m_slab + 4 * g + r, M - 1)];
     }
@@ -535,7 +606,8 @@ void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const v
   if (M <= 0) return;
   if (prec == P_F32) launch_prec<P_F32>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
   else if (prec == P_BF16) launch_prec<P_BF16>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
-  else launch_prec<P_I8>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+  else if (prec == P_I8) launch_prec<P_I8>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+  else launch_prec<P_I4>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
 }
 
 void launch_gemm_splitk(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
@@ -549,9 +621,12 @@ void launch_gemm_splitk(int prec, const void* A, const float* a_scale, const voi
   } else if (prec == P_BF16) {
     if (long_k) go<P_BF16, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
     else go<P_BF16, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
-  } else {
+  } else if (prec == P_I8) {
     if (long_k) go<P_I8, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
     else go<P_I8, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+  } else {
+    if (long_k) go<P_I4, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    else go<P_I4, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
   }
 }
 
@@ -561,7 +636,8 @@ void launch_gemm_qkv(int prec, const void* A, const float* a_scale, const void* 
   if (prec == P_F32) launch_qkv_prec<P_F32, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
   else if (prec == P_BF16 && out_kind == O_BF16) launch_qkv_prec<P_BF16, O_BF16>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
   else if (prec == P_BF16) launch_qkv_prec<P_BF16, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
-  else launch_qkv_prec<P_I8, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
+  else if (prec == P_I8) launch_qkv_prec<P_I8, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
+  else launch_qkv_prec<P_I4, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
 }
 
 }  // namespace tte

@@ -52,7 +52,7 @@ Layout layout_of(const tte_config& c) {
     return at;
   };
   L.x = take(T * H * 4);
-  L.xa = take(c.precision == TTE_INT8 ? T * (H > I ? H : I) : T * H * ab);
+  L.xa = take(c.precision >= TTE_INT8 ? T * (H > I ? H : I) : T * H * ab);
   L.ascale = take(T * 4);
   L.qkv = take(T * 3 * H * ab);
   // V transposed, [H][vt_stride]: 64 tokens of slack so a key tile that
@@ -81,7 +81,10 @@ bool check_config(const tte_config* c, std::string* why) {
     return false;
   };
   if (!c) return bad("config is NULL");
-  if (c->precision < TTE_FP32 || c->precision > TTE_INT8) return bad("precision must be TTE_FP32, TTE_BF16 or TTE_INT8");
+  if (c->precision < TTE_FP32 || c->precision > TTE_INT4)
+    return bad("precision must be TTE_FP32, TTE_BF16, TTE_INT8 or TTE_INT4");
+  if (c->precision == TTE_INT4 && (c->hidden % 256 != 0 || c->intermediate % 256 != 0))
+    return bad("TTE_INT4 needs hidden and intermediate multiples of 256 (whole 4-bit super-blocks)");
   if (c->vocab <= 0 || c->n_layers <= 0 || c->n_heads <= 0) return bad("vocab, n_layers and n_heads must be positive");
   if (c->head_dim != 64) return bad("head_dim must be 64");
   if (c->hidden != c->n_heads * c->head_dim) return bad("hidden must equal n_heads * head_dim");
@@ -257,8 +260,8 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
   const size_t state_bytes = (size_t)T * H * 4;
   {
     ProfScope ps(m, TTE_K_EMBED, s);
-    launch_embed_ln(P, d_ids, T, m->w.tok_emb, m->w.tok_emb_scale, c.vocab, m->w.emb_norm, c.ln_eps, H, m->d_off, B,
-                    m->x, m->seg, s);
+    launch_embed_ln(P == TTE_INT4 ? TTE_INT8 : P, d_ids, T, m->w.tok_emb, m->w.tok_emb_scale, c.vocab, m->w.emb_norm,
+                    c.ln_eps, H, m->d_off, B, m->x, m->seg, s);
   }
   if (d_states) (void)hipMemcpyAsync(d_states, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
 
@@ -269,7 +272,8 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
   const int o2_splits =
       ((c.flags & TTE_FLAG_SPLIT_K) && I >= 2048 && ((T + 63) / 64) * (H / 128) < 256) ? 2 : 1;
   bool pending = false;  // x still lacks the partials of the last down-projection
-  const int in_fmt = P == TTE_INT8 ? O_I8 : act;
+  const bool integer = P == TTE_INT8 || P == TTE_INT4;  // 7-bit activation codes into the weight products
+  const int in_fmt = integer ? O_I8 : act;
   for (int l = 0; l < n_run; ++l) {
     const tte_layer_weights& LW = m->layers[l];
     const int glob = (l % c.global_every) == 0;
@@ -282,7 +286,7 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
       launch_resid_ln(m->x, m->kpart, o2_splits, LW.attn_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
       pending = false;
     } else {
-      ProfScope ps(m, P == TTE_INT8 && l == 0 ? TTE_K_QUANT : TTE_K_NORM, s);
+      ProfScope ps(m, integer && l == 0 ? TTE_K_QUANT : TTE_K_NORM, s);
       launch_ln(m->x, l == 0 ? nullptr : LW.attn_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
     }
     {
@@ -296,7 +300,7 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
                        c.window, s);
     }
     const void* o_in = m->o;
-    if (P == TTE_INT8) {
+    if (integer) {
       ProfScope ps(m, TTE_K_QUANT, s);
       launch_quant7(reinterpret_cast<const float*>(m->o), T, H, reinterpret_cast<int8_t*>(m->xa), m->ascale, s);
       o_in = m->xa;
@@ -314,7 +318,7 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
       launch_gemm(P, E_GEGLU, m->xa, m->ascale, LW.wi, LW.wi_scale, T, I, H, m->y, act, s);
     }
     const void* y_in = m->y;
-    if (P == TTE_INT8) {
+    if (integer) {
       ProfScope ps(m, TTE_K_QUANT, s);
       launch_quant7(reinterpret_cast<const float*>(m->y), T, I, reinterpret_cast<int8_t*>(m->xa), m->ascale, s);
       y_in = m->xa;
@@ -373,7 +377,7 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   if (!w || !out) return fail(TTE_E_INVALID, "weights or out is NULL");
   *out = nullptr;
   const tte_config& c = *cfg;
-  const bool q = c.precision == TTE_INT8;
+  const bool q = c.precision == TTE_INT8 || c.precision == TTE_INT4;
   if (!w->tok_emb || !w->emb_norm || !w->final_norm || !w->layers || (q && !w->tok_emb_scale))
     return fail(TTE_E_INVALID, "a required weight pointer is NULL");
   for (int l = 0; l < c.n_layers; ++l) {
@@ -381,7 +385,7 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
     if (!L.wqkv || !L.wo || !L.wi || !L.wo2 || !L.mlp_norm || (l > 0 && !L.attn_norm))
       return fail(TTE_E_INVALID, "layer " + std::to_string(l) + ": a required weight pointer is NULL");
     if (q && (!L.wqkv_scale || !L.wo_scale || !L.wi_scale || !L.wo2_scale))
-      return fail(TTE_E_INVALID, "layer " + std::to_string(l) + ": an int8 scale pointer is NULL");
+      return fail(TTE_E_INVALID, "layer " + std::to_string(l) + ": a scale / record pointer is NULL");
   }
   int ndev = 0;
   if (hipGetDeviceCount(&ndev) != hipSuccess || ndev <= 0) {
@@ -523,7 +527,7 @@ tte_status tte_op_quant7(const float* d_x, int32_t rows, int32_t width, int8_t* 
 tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, const float* d_a_scale, const void* d_w,
                        const float* d_w_scale, int32_t M, int32_t N, int32_t K, void* d_c, int32_t out_kind,
                        void* stream) {
-  if (precision < TTE_FP32 || precision > TTE_INT8) return fail(TTE_E_INVALID, "bad precision");
+  if (precision < TTE_FP32 || precision > TTE_INT4) return fail(TTE_E_INVALID, "bad precision");
   if (epilogue < TTE_EPI_STORE || epilogue > TTE_EPI_GEGLU) return fail(TTE_E_INVALID, "bad epilogue");
   if (M < 0 || N <= 0 || K <= 0) return fail(TTE_E_INVALID, "M must be >= 0, N and K > 0");
   if (K % 128 != 0) return fail(TTE_E_UNSUPPORTED, "K must be a multiple of 128");
@@ -533,7 +537,8 @@ tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, con
   if (epilogue == TTE_EPI_RESIDUAL && out_kind != TTE_OUT_F32) return fail(TTE_E_INVALID, "RESIDUAL needs fp32 C");
   if (M == 0) return TTE_OK;
   if (!d_a || !d_w || !d_c) return fail(TTE_E_INVALID, "NULL buffer");
-  if (precision == TTE_INT8 && (!d_a_scale || !d_w_scale)) return fail(TTE_E_INVALID, "int8 needs both scales");
+  if (precision >= TTE_INT8 && (!d_a_scale || !d_w_scale)) return fail(TTE_E_INVALID, "int8 / int4 need both scales");
+  if (precision == TTE_INT4 && K % 256 != 0) return fail(TTE_E_UNSUPPORTED, "TTE_INT4 needs K a multiple of 256");
   (void)hipGetLastError();
   launch_gemm(precision, epilogue, d_a, d_a_scale, d_w, d_w_scale, M, N, K, d_c, out_kind,
               reinterpret_cast<hipStream_t>(stream));
@@ -543,13 +548,14 @@ tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, con
 tte_status tte_op_gemm_splitk(int32_t precision, const void* d_a, const float* d_a_scale, const void* d_w,
                               const float* d_w_scale, int32_t M, int32_t N, int32_t K, int32_t splits,
                               float* d_partials, void* stream) {
-  if (precision < TTE_FP32 || precision > TTE_INT8) return fail(TTE_E_INVALID, "bad precision");
+  if (precision < TTE_FP32 || precision > TTE_INT4) return fail(TTE_E_INVALID, "bad precision");
   if (M < 0 || N <= 0 || K <= 0 || splits < 1) return fail(TTE_E_INVALID, "M must be >= 0, N, K, splits > 0");
   const int es = precision == TTE_FP32 ? 4 : (precision == TTE_BF16 ? 2 : 1);
   if (N % 128 != 0 || K % splits != 0 || ((K / splits) * es) % 128 != 0)
     return fail(TTE_E_UNSUPPORTED, "N must be a multiple of 128 and each K part a multiple of 128 bytes");
+  if (precision == TTE_INT4 && K % 256 != 0) return fail(TTE_E_UNSUPPORTED, "TTE_INT4 needs K a multiple of 256");
   if (M == 0) return TTE_OK;
-  if (!d_a || !d_w || !d_partials || (precision == TTE_INT8 && (!d_a_scale || !d_w_scale)))
+  if (!d_a || !d_w || !d_partials || (precision >= TTE_INT8 && (!d_a_scale || !d_w_scale)))
     return fail(TTE_E_INVALID, "NULL buffer");
   (void)hipGetLastError();
   launch_gemm_splitk(precision, d_a, d_a_scale, d_w, d_w_scale, M, N, K, splits, d_partials,
@@ -601,7 +607,7 @@ tte_status tte_op_qkv(tte_model* m, int32_t layer, const void* d_a, const float*
   tte_status st = check_pack(m->cfg, n_tokens, h_offsets, n_texts);
   if (st != TTE_OK) return st;
   if (n_texts == 0) return TTE_OK;
-  if (!d_a || !d_qk || !d_vt || (m->cfg.precision == TTE_INT8 && !d_a_scale)) return fail(TTE_E_INVALID, "NULL buffer");
+  if (!d_a || !d_qk || !d_vt || (m->cfg.precision >= TTE_INT8 && !d_a_scale)) return fail(TTE_E_INVALID, "NULL buffer");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   int n_units = 0;
