@@ -126,6 +126,8 @@ def main():
                     help="pooled unit vectors per text (tte_embed) or per-token states (tte_embed_tokens)")
     ap.add_argument("--split-k", action="store_true",
                     help="TTE_FLAG_SPLIT_K: split the down-projection of short packs (lower single-call latency)")
+    ap.add_argument("--graph", action="store_true",
+                    help="TTE_FLAG_GRAPH: replay each pack's captured HIP graph (needs --warmup >= 2)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=3000)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
@@ -175,9 +177,10 @@ def main():
     max_tokens = max(p.n_tokens for p in packs)
     S = max(1, a.streams)
     model = Model(cfg, w, max_tokens=max_tokens, max_text_len=max(max_tokens, 512), max_texts=1024, device="cuda:0",
-                  split_k=a.split_k)
+                  split_k=a.split_k, graph=a.graph)
     models = [model] + [Model(cfg, None, max_tokens=max_tokens, max_text_len=max(max_tokens, 512), max_texts=1024,
-                              device="cuda:0", shared_from=model, split_k=a.split_k) for _ in range(S - 1)]
+                              device="cuda:0", shared_from=model, split_k=a.split_k, graph=a.graph)
+                        for _ in range(S - 1)]
     streams = [torch.cuda.Stream(device=dev) for _ in range(S)]
     ids = [torch.from_numpy(p.ids).to(dev) for p in packs]
     per_token = a.output == "tokens"
@@ -271,7 +274,9 @@ def main():
         "config": {"workload": a.workload, "packs_per_step": len(packs), "tokens_per_step": tokens_per_step,
                    "pack_budget": spec.get("pack_budget"), "layers": cfg.layers, "hidden": cfg.hidden,
                    "heads": cfg.heads, "intermediate": cfg.intermediate, "calls_per_step": len(packs),
-                   "streams": S, "hw_queues": int(os.environ.get("GPU_MAX_HW_QUEUES", "4")), "output": a.output, "split_k": a.split_k, "single_stream_ms_per_step": round(single_ms, 3) if single_ms else None},
+                   "streams": S, "hw_queues": int(os.environ.get("GPU_MAX_HW_QUEUES", "4")), "output": a.output,
+                   "split_k": a.split_k, "graph": a.graph,
+                   "single_stream_ms_per_step": round(single_ms, 3) if single_ms else None},
         "roofline": roofline,
     }
     if breakdown is not None:

@@ -75,7 +75,22 @@ typedef enum {
    * call by about 5%.  It costs 2 * max_tokens * H * 4 bytes of workspace
    * and extra HBM traffic, which lowers throughput when several calls
    * already share the GPU on concurrent streams, so it is off by default. */
-  TTE_FLAG_SPLIT_K = 1
+  TTE_FLAG_SPLIT_K = 1,
+  /* HIP-graph replay of the pass (the page's section on batching keeps a
+   * pool of graphs keyed by batch size; here the key is the pack's shape).
+   * tte_embed and tte_embed_tokens record, per model, the shapes
+   * (n_tokens, n_texts, pool units = sum over texts of ceil(len / 32),
+   * output kind) they are called with; at a shape's second call on a
+   * non-null stream the kernel sequence is captured into a graph, which
+   * that call and every later call of the shape replay with one launch.
+   * The token ids and output pointers travel with the offsets upload and
+   * are read by the kernels from device memory, so a replay takes the
+   * call's own buffers.  At most 64 shapes per model are kept (the least
+   * recently used is dropped).  Results are bit-identical to the eager
+   * pass.  Calls on the null stream, tte_embed_trace and calls made while
+   * tte_profile_start is active run eagerly.  A graph baked with a
+   * model's workspace must not outlive it: tte_destroy releases them. */
+  TTE_FLAG_GRAPH = 2
 } tte_flag;
 
 /* Model shape and limits.  Defaults in parentheses are the page's values. */
@@ -272,6 +287,14 @@ tte_status tte_profile_start(tte_model* m, uint32_t class_mask, int32_t max_laun
  * time in milliseconds and the number of timed launches (arrays of
  * TTE_K_COUNT entries).  Stops recording. */
 tte_status tte_profile_stop(tte_model* m, double* ms_per_class, int64_t* launches_per_class);
+
+/* TTE_FLAG_GRAPH bookkeeping of a model (host counters, no GPU work):
+ * *n_shapes = pack shapes currently recorded, *n_graphs = those with an
+ * instantiated graph, *n_replays = graph launches since tte_create (the
+ * call that captures a shape counts as its first replay).  All three are
+ * 0 for a model without the flag.  Returns TTE_E_INVALID on NULL
+ * arguments. */
+tte_status tte_graph_stats(const tte_model* m, int32_t* n_shapes, int32_t* n_graphs, int64_t* n_replays);
 
 #ifdef __cplusplus
 }

@@ -47,9 +47,16 @@ def test_split_k_flag_adds_partials_workspace(lib):
     assert b - a == 2 * 2048 * 768 * 4  # two fp32 partial products [max_tokens, H]
 
 
+def test_graph_flag_accepted_without_extra_workspace(lib):
+    """TTE_FLAG_GRAPH keeps its graphs host-side: the workspace is the same."""
+    assert B.tte_workspace_size(_cfg(flags=B.TTE_FLAG_GRAPH)) == B.tte_workspace_size(_cfg())
+    assert B.tte_workspace_size(_cfg(flags=B.TTE_FLAG_GRAPH | B.TTE_FLAG_SPLIT_K)) == \
+        B.tte_workspace_size(_cfg(flags=B.TTE_FLAG_SPLIT_K))
+
+
 @pytest.mark.parametrize("field,value", [
     ("head_dim", 32), ("hidden", 700), ("intermediate", 3000), ("precision", 7), ("max_tokens", 0),
-    ("global_every", 0), ("window", -1), ("ln_eps", 0.0), ("n_layers", 0), ("max_texts", 0), ("flags", 2)])
+    ("global_every", 0), ("window", -1), ("ln_eps", 0.0), ("n_layers", 0), ("max_texts", 0), ("flags", 4)])
 def test_bad_configs_rejected(lib, field, value):
     c = _cfg(**{field: value})
     n = ctypes.c_size_t(0)

@@ -28,10 +28,11 @@ def similarity(emb_dev, stream=None):
 
 
 def make_config(spec, max_tokens: int, max_text_len: int, max_texts: Optional[int] = None,
-                split_k: bool = False) -> B.tte_config:
+                split_k: bool = False, graph: bool = False) -> B.tte_config:
     """tte_config from a dict / dataclass with the encoder's shape fields.
     split_k sets TTE_FLAG_SPLIT_K (lower latency of one call on an idle GPU,
-    lower throughput under concurrent calls)."""
+    lower throughput under concurrent calls); graph sets TTE_FLAG_GRAPH
+    (per-shape HIP-graph replay on non-null streams)."""
     d = spec if isinstance(spec, dict) else spec.as_dict()
     return B.tte_config(
         vocab=d["vocab"], hidden=d["hidden"], n_heads=d["heads"], head_dim=d["head_dim"],
@@ -40,7 +41,8 @@ def make_config(spec, max_tokens: int, max_text_len: int, max_texts: Optional[in
         rope_base_local=d.get("rope_base_local", 10000.0), ln_eps=d.get("ln_eps", 1e-5),
         max_tokens=max_tokens, max_text_len=max_text_len,
         max_texts=max_texts if max_texts is not None else max_tokens,
-        precision=B.PRECISIONS[d["precision"]], flags=B.TTE_FLAG_SPLIT_K if split_k else 0)
+        precision=B.PRECISIONS[d["precision"]],
+        flags=(B.TTE_FLAG_SPLIT_K if split_k else 0) | (B.TTE_FLAG_GRAPH if graph else 0))
 
 
 class Model:
@@ -53,13 +55,13 @@ class Model:
 
     def __init__(self, spec, weights: dict, max_tokens: int = 2048, max_text_len: Optional[int] = None,
                  max_texts: Optional[int] = None, device: str = "cuda:0", shared_from: "Model" = None,
-                 split_k: bool = False):
+                 split_k: bool = False, graph: bool = False):
         import torch
         self.torch = torch
         B.lib()
         self.device = torch.device(device)
         self.spec = spec if isinstance(spec, dict) else spec.as_dict()
-        self.cfg = make_config(self.spec, max_tokens, max_text_len or max_tokens, max_texts, split_k)
+        self.cfg = make_config(self.spec, max_tokens, max_text_len or max_tokens, max_texts, split_k, graph)
         self.precision = self.spec["precision"]
         if shared_from is not None:
             self._keep = shared_from._keep

@@ -16,7 +16,7 @@ HEADER = os.path.join(os.path.dirname(PKG), "include", "tte.h")
 TTE_OK, TTE_E_INVALID, TTE_E_UNSUPPORTED, TTE_E_NOMEM, TTE_E_DEVICE = range(5)
 STATUS_NAMES = {0: "TTE_OK", 1: "TTE_E_INVALID", 2: "TTE_E_UNSUPPORTED", 3: "TTE_E_NOMEM", 4: "TTE_E_DEVICE"}
 TTE_FP32, TTE_BF16, TTE_INT8, TTE_INT4 = 0, 1, 2, 3
-TTE_FLAG_SPLIT_K = 1
+TTE_FLAG_SPLIT_K, TTE_FLAG_GRAPH = 1, 2
 PRECISIONS = {"fp32": TTE_FP32, "bf16": TTE_BF16, "int8": TTE_INT8, "int4": TTE_INT4}
 TTE_OUT_F32, TTE_OUT_BF16, TTE_OUT_I8 = 0, 1, 2
 TTE_EPI_STORE, TTE_EPI_RESIDUAL, TTE_EPI_GEGLU = 0, 1, 2
@@ -71,6 +71,7 @@ _SIGS = {
     "tte_op_pool": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p, c_void_p]),
     "tte_profile_start": (c_int32, [c_void_p, c_uint32, c_int32]),
     "tte_profile_stop": (c_int32, [c_void_p, POINTER(c_double), POINTER(c_int64)]),
+    "tte_graph_stats": (c_int32, [c_void_p, POINTER(c_int32), POINTER(c_int32), POINTER(c_int64)]),
 }
 
 _lib = None
@@ -216,6 +217,13 @@ def tte_op_pool(model: int, d_x: int, n_tokens: int, offsets, d_out: int, stream
 
 def tte_profile_start(model: int, class_mask: int, max_launches: int) -> None:
     check(lib().tte_profile_start(c_void_p(model), class_mask, max_launches))
+
+
+def tte_graph_stats(model: int):
+    """(shapes recorded, graphs instantiated, graph launches) of a model."""
+    a, b, c = c_int32(0), c_int32(0), c_int64(0)
+    check(lib().tte_graph_stats(c_void_p(model), ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
 
 
 def tte_profile_stop(model: int):

@@ -32,6 +32,15 @@ struct QkvOut {
   int hidden;
 };
 
+// Pointers of one embedding call kept in device memory, so that a replayed
+// graph of the pass reads the call's token ids and writes its output
+// wherever the caller's buffers are.  Launchers take it nullable: with
+// io == nullptr the kernels use the pointers they are given.
+struct PackIO {
+  const int32_t* ids;
+  float* out;
+};
+
 // Row widths (H or I) the row kernels handle: multiples of 64 with
 // width/64 in this set.
 bool row_width_supported(int width);
@@ -39,14 +48,14 @@ bool row_width_supported(int width);
 // Gather rows of the token table (fp32, bf16, or int8 blocks with fp32
 // scales), bias-free LayerNorm with gain `gamma`, write fp32 x [T, H].
 // Also writes seg[t] from the device copy of the offsets.
-void launch_embed_ln(int prec, const int32_t* ids, int T, const void* table, const float* table_scale,
-                     int vocab, const float* gamma, float eps, int H, const int* d_off, int n_texts, float* x,
-                     Seg* seg, hipStream_t s);
+void launch_embed_ln(int prec, const int32_t* ids, const PackIO* io, int T, const void* table,
+                     const float* table_scale, int vocab, const float* gamma, float eps, int H, const int* d_off,
+                     int n_texts, float* x, Seg* seg, hipStream_t s);
 
 // Bias-free LayerNorm (gamma non-null) or plain conversion (gamma null) of
 // fp32 rows to fp32 / bf16 / 7-bit int8 codes + row scales.
 void launch_ln(const float* x, const float* gamma, int rows, int width, float eps, int out_kind, void* out,
-               float* out_scale, hipStream_t s);
+               float* out_scale, hipStream_t s, const PackIO* io = nullptr);
 
 // Per-row 7-bit quantisation.
 void launch_quant7(const float* x, int rows, int width, int8_t* q, float* scale, hipStream_t s);
@@ -94,6 +103,6 @@ void launch_similarity(const float* e, int n, int dim, float* sim, hipStream_t s
 // one text: unit_start[b] .. unit_start[b+1] belong to text b.
 constexpr int POOL_ROWS = 32;
 void launch_pool(const float* x, const float* gamma, float eps, int H, const int* d_off, const int* d_unit,
-                 int n_texts, int n_units, float* partial, float* out, hipStream_t s);
+                 int n_texts, int n_units, float* partial, float* out, hipStream_t s, const PackIO* io = nullptr);
 
 }  // namespace tte

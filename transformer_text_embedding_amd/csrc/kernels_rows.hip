@@ -125,8 +125,8 @@ __device__ __forceinline__ void layernorm_regs(float (&v)[EPL], const float* __r
 // --------------------------------------------------------------------------
 
 template <int EPL, int PREC>
-__global__ __launch_bounds__(256) void k_embed_ln(const int32_t* __restrict__ ids, int T,
-                                                  const void* __restrict__ table,
+__global__ __launch_bounds__(256) void k_embed_ln(const int32_t* __restrict__ ids, const PackIO* __restrict__ io,
+                                                  int T, const void* __restrict__ table,
                                                   const float* __restrict__ table_scale, int vocab,
                                                   const float* __restrict__ gamma, float eps,
                                                   const int* __restrict__ off, int n_texts,
@@ -136,6 +136,7 @@ __global__ __launch_bounds__(256) void k_embed_ln(const int32_t* __restrict__ id
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  if (io) ids = io->ids;
   int id = ids[t];
   id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
   float v[EPL];
@@ -177,12 +178,14 @@ __global__ __launch_bounds__(256) void k_embed_ln(const int32_t* __restrict__ id
 
 template <int EPL, int OUT, bool NORM>
 __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ x, const float* __restrict__ gamma, int rows,
-                                            float eps, void* __restrict__ out, float* __restrict__ out_scale) {
+                                            float eps, void* __restrict__ out, float* __restrict__ out_scale,
+                                            const PackIO* __restrict__ io) {
   using RS = RowShape<EPL>;
   constexpr int Wd = RS::W;
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
+  if (io) out = io->out;
   float v[EPL];
   load_f32_row<EPL>(x + (size_t)r * Wd, lane, v);
   if constexpr (NORM) layernorm_regs<EPL>(v, gamma, lane, eps);
@@ -281,10 +284,12 @@ __global__ __launch_bounds__(256) void k_pool_partial(const float* __restrict__ 
 // count, divide by max(||e||, 1e-12).
 template <int H>
 __global__ __launch_bounds__(256) void k_pool_finish(const float* __restrict__ partial, const int* __restrict__ off,
-                                                     const int* __restrict__ unit_start, float* __restrict__ out) {
+                                                     const int* __restrict__ unit_start, float* __restrict__ out,
+                                                     const PackIO* __restrict__ io) {
   constexpr int PER = (H + 255) / 256;
   __shared__ float red[4];
   const int b = blockIdx.x;
+  if (io) out = io->out;
   const int u0 = unit_start[b], u1 = unit_start[b + 1];
   const float inv_n = 1.f / (float)(off[b + 1] - off[b]);
   float e[PER];
@@ -336,37 +341,38 @@ bool row_width_supported(int width) {
     default: break;                    \
   }
 
-void launch_embed_ln(int prec, const int32_t* ids, int T, const void* table, const float* table_scale, int vocab,
-                     const float* gamma, float eps, int H, const int* d_off, int n_texts, float* x, Seg* seg,
+void launch_embed_ln(int prec, const int32_t* ids, const PackIO* io, int T, const void* table, const float* table_scale,
+                     int vocab, const float* gamma, float eps, int H, const int* d_off, int n_texts, float* x, Seg* seg,
                      hipStream_t s) {
   if (T <= 0) return;
   const dim3 grid((T + 3) / 4), block(256);
 #define L_EMB(E)                                                                                                    \
   if (prec == P_F32)                                                                                                \
-    k_embed_ln<E, P_F32><<<grid, block, 0, s>>>(ids, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x,   \
-                                                 seg);                                                              \
+    k_embed_ln<E, P_F32><<<grid, block, 0, s>>>(ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, \
+                                                 x, seg);                                                           \
   else if (prec == P_BF16)                                                                                          \
-    k_embed_ln<E, P_BF16><<<grid, block, 0, s>>>(ids, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x,  \
-                                                  seg);                                                             \
+    k_embed_ln<E, P_BF16><<<grid, block, 0, s>>>(ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, \
+                                                  x, seg);                                                          \
   else                                                                                                              \
-    k_embed_ln<E, P_I8><<<grid, block, 0, s>>>(ids, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x, seg);
+    k_embed_ln<E, P_I8><<<grid, block, 0, s>>>(ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x, \
+                                                seg);
   TTE_EPL_DISPATCH(H, L_EMB)
 #undef L_EMB
 }
 
 void launch_ln(const float* x, const float* gamma, int rows, int width, float eps, int out_kind, void* out,
-               float* out_scale, hipStream_t s) {
+               float* out_scale, hipStream_t s, const PackIO* io) {
   if (rows <= 0) return;
   const dim3 grid((rows + 3) / 4), block(256);
 #define L_LN(E)                                                                                        \
   if (gamma) {                                                                                         \
-    if (out_kind == O_F32) k_ln<E, O_F32, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale);   \
-    else if (out_kind == O_BF16) k_ln<E, O_BF16, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale); \
-    else k_ln<E, O_I8, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale);              \
+    if (out_kind == O_F32) k_ln<E, O_F32, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io);   \
+    else if (out_kind == O_BF16) k_ln<E, O_BF16, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io); \
+    else k_ln<E, O_I8, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io);              \
   } else {                                                                                             \
-    if (out_kind == O_F32) k_ln<E, O_F32, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale);  \
-    else if (out_kind == O_BF16) k_ln<E, O_BF16, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale); \
-    else k_ln<E, O_I8, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale);             \
+    if (out_kind == O_F32) k_ln<E, O_F32, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io);  \
+    else if (out_kind == O_BF16) k_ln<E, O_BF16, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io); \
+    else k_ln<E, O_I8, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io);             \
   }
   TTE_EPL_DISPATCH(width, L_LN)
 #undef L_LN
@@ -403,11 +409,11 @@ void launch_resid_ln(float* x, const float* partials, int splits, const float* g
 }
 
 void launch_pool(const float* x, const float* gamma, float eps, int H, const int* d_off, const int* d_unit,
-                 int n_texts, int n_units, float* partial, float* out, hipStream_t s) {
+                 int n_texts, int n_units, float* partial, float* out, hipStream_t s, const PackIO* io) {
   if (n_texts <= 0) return;
 #define L_POOL(E)                                                                                          \
   k_pool_partial<E><<<n_units, 256, 0, s>>>(x, gamma, eps, d_off, d_unit, n_texts, partial);               \
-  k_pool_finish<E * 64><<<n_texts, 256, 0, s>>>(partial, d_off, d_unit, out);
+  k_pool_finish<E * 64><<<n_texts, 256, 0, s>>>(partial, d_off, d_unit, out, io);
   TTE_EPL_DISPATCH(H, L_POOL)
 #undef L_POOL
 }

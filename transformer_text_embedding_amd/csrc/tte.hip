@@ -33,7 +33,7 @@ tte_status fail(tte_status s, const std::string& msg) {
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
 struct Layout {
-  size_t x, xa, ascale, qkv, vt, o, y, kpart, seg, off, unit, partial, cosg, sing, cosl, sinl, total;
+  size_t x, xa, ascale, qkv, vt, o, y, kpart, seg, off, partial, cosg, sing, cosl, sinl, total;
   int max_units;
   int vt_stride;
 };
@@ -63,8 +63,8 @@ Layout layout_of(const tte_config& c) {
   L.y = take(T * I * ab);
   L.kpart = take(c.flags & TTE_FLAG_SPLIT_K ? 2 * T * H * 4 : 0);  // split-K partials of the down-projection
   L.seg = take(T * sizeof(Seg));
-  L.off = take(((size_t)c.max_texts + 1) * 4);
-  L.unit = take(((size_t)c.max_texts + 1) * 4);
+  // the call's PackIO, then its offsets and pool-unit starts back to back
+  L.off = take(sizeof(PackIO) + 2 * ((size_t)c.max_texts + 1) * 4);
   L.partial = take((size_t)L.max_units * H * 4);
   const size_t rope = (size_t)c.max_text_len * 32 * 4;
   L.cosg = take(rope);
@@ -99,7 +99,7 @@ bool check_config(const tte_config* c, std::string* why) {
   if (c->max_tokens <= 0 || c->max_text_len <= 0 || c->max_texts <= 0)
     return bad("max_tokens, max_text_len and max_texts must be positive");
   if (c->max_tokens > (1 << 24)) return bad("max_tokens above 2^24");
-  if (c->flags & ~int32_t(TTE_FLAG_SPLIT_K)) return bad("unknown flag");
+  if (c->flags & ~int32_t(TTE_FLAG_SPLIT_K | TTE_FLAG_GRAPH)) return bad("unknown flag");
   return true;
 }
 
@@ -141,8 +141,9 @@ struct tte_model {
   void* y;
   float* kpart;
   Seg* seg;
+  PackIO* d_io;  // the call's ids / output pointers (read by graph replays)
   int* d_off;
-  int* d_unit;
+  int* d_unit;   // d_off + n_texts + 1 of the last upload
   float* partial;
   const float *cosg, *sing, *cosl, *sinl;
   // pinned staging for the per-call offsets upload: a ring of slots, each
@@ -158,6 +159,16 @@ struct tte_model {
   std::vector<int> ev_cls;
   int ev_used;
   bool ev_overflow;
+  // TTE_FLAG_GRAPH: pack shapes seen, and the graphs of those seen twice
+  struct GraphEntry {
+    int kind, T, B, units;
+    hipGraphExec_t exec;  // null until the shape's second call
+    bool failed;          // capture did not succeed: run eagerly
+    uint64_t used;
+  };
+  std::vector<GraphEntry> graphs;
+  uint64_t graph_clock;
+  int64_t graph_replays;
 };
 
 namespace {
@@ -186,11 +197,15 @@ tte_status hip_check(hipError_t e, const char* what) {
   return fail(TTE_E_DEVICE, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// Copies offsets and pool-unit starts into the workspace (stream-ordered,
-// from pinned staging that is reused only once the previous copy is done).
+// Copies the call's PackIO, offsets and pool-unit starts into the
+// workspace in one stream-ordered copy, from pinned staging that is reused
+// only once the previous copy from it is done.  Sets m->d_unit.
 constexpr int STAGE_SLOTS = 8;
 
-tte_status upload_pack(tte_model* m, const int32_t* h_off, int n_texts, int* n_units, hipStream_t s) {
+size_t stage_ints(const tte_config& c) { return sizeof(PackIO) / 4 + 2 * ((size_t)c.max_texts + 1); }
+
+tte_status upload_pack(tte_model* m, const int32_t* h_off, int n_texts, int* n_units, hipStream_t s,
+                       const int32_t* d_ids = nullptr, float* d_out = nullptr) {
   const int slot = m->stage_next;
   m->stage_next = (slot + 1) % STAGE_SLOTS;
   if (m->stage_pending[slot]) {
@@ -198,17 +213,18 @@ tte_status upload_pack(tte_model* m, const int32_t* h_off, int n_texts, int* n_u
     if (st != TTE_OK) return st;
     m->stage_pending[slot] = false;
   }
-  int* so = m->h_stage + (size_t)slot * 2 * (m->cfg.max_texts + 1);
-  int* su = so + (m->cfg.max_texts + 1);
+  int* base = m->h_stage + (size_t)slot * stage_ints(m->cfg);
+  const PackIO io{d_ids, d_out};
+  std::memcpy(base, &io, sizeof(PackIO));
+  int* so = base + sizeof(PackIO) / 4;
+  int* su = so + (n_texts + 1);
   std::memcpy(so, h_off, sizeof(int) * (size_t)(n_texts + 1));
   su[0] = 0;
   for (int b = 0; b < n_texts; ++b) su[b + 1] = su[b] + (h_off[b + 1] - h_off[b] + POOL_ROWS - 1) / POOL_ROWS;
   *n_units = su[n_texts];
-  tte_status st = hip_check(hipMemcpyAsync(m->d_off, so, sizeof(int) * (n_texts + 1), hipMemcpyHostToDevice, s),
-                            "hipMemcpyAsync(offsets)");
-  if (st != TTE_OK) return st;
-  st = hip_check(hipMemcpyAsync(m->d_unit, su, sizeof(int) * (n_texts + 1), hipMemcpyHostToDevice, s),
-                 "hipMemcpyAsync(units)");
+  m->d_unit = m->d_off + (n_texts + 1);
+  const size_t bytes = sizeof(PackIO) + sizeof(int) * 2 * (size_t)(n_texts + 1);
+  tte_status st = hip_check(hipMemcpyAsync(m->d_io, base, bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync(offsets)");
   if (st != TTE_OK) return st;
   st = hip_check(hipEventRecord(m->stage_ev[slot], s), "hipEventRecord");
   if (st != TTE_OK) return st;
@@ -229,39 +245,23 @@ __global__ void k_seg(const int* __restrict__ off, int n_texts, int T, Seg* __re
   seg[t] = Seg{off[lo], off[lo + 1]};
 }
 
-// One pass over a pack.  The output is either the pooled unit vectors
-// (d_out [B, H]) or, with d_tok, the per-token states after the final
-// LayerNorm ([T, H]).
-tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t* h_off, int32_t B, float* d_out,
-                    float* d_states, int32_t n_dump, void* stream, float* d_tok = nullptr) {
-  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+// The launch sequence of one pass over an uploaded pack.  The output is
+// either the pooled unit vectors (d_out [B, H]) or, with d_tok, the
+// per-token states after the final LayerNorm ([T, H]); d_states receives
+// the residual stream after the embedding norm and each of the first n_run
+// layers.  With io non-null the embedding and output kernels take the ids
+// and output pointers from it (device memory) instead of d_ids / d_out /
+// d_tok.
+void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t T, int32_t B, int n_units,
+                  float* d_out, float* d_states, int n_run, float* d_tok, hipStream_t s) {
   const tte_config& c = m->cfg;
-  tte_status st = check_pack(c, T, h_off, B);
-  if (st != TTE_OK) return st;
-  if (B == 0) return TTE_OK;
-  if (!d_ids) return fail(TTE_E_INVALID, "d_token_ids is NULL");
-  if (d_states) {
-    if (n_dump < 0 || n_dump > c.n_layers) return fail(TTE_E_INVALID, "n_dump must be in [0, n_layers]");
-  } else {
-    n_dump = -1;
-  }
-  const int n_run = (d_states && n_dump < c.n_layers) ? n_dump : c.n_layers;
-  if (n_run == c.n_layers && !d_out && !d_tok) return fail(TTE_E_INVALID, "d_out is NULL");
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-  st = hip_check(hipSetDevice(m->device), "hipSetDevice");
-  if (st != TTE_OK) return st;
-  (void)hipGetLastError();
-  int n_units = 0;
-  st = upload_pack(m, h_off, B, &n_units, s);
-  if (st != TTE_OK) return st;
-
   const int P = c.precision, H = c.hidden, I = c.intermediate, nh = c.n_heads;
   const int act = P == TTE_BF16 ? O_BF16 : O_F32;  // format of qkv / o / y
   const size_t state_bytes = (size_t)T * H * 4;
   {
     ProfScope ps(m, TTE_K_EMBED, s);
-    launch_embed_ln(P == TTE_INT4 ? TTE_INT8 : P, d_ids, T, m->w.tok_emb, m->w.tok_emb_scale, c.vocab, m->w.emb_norm,
-                    c.ln_eps, H, m->d_off, B, m->x, m->seg, s);
+    launch_embed_ln(P == TTE_INT4 ? TTE_INT8 : P, d_ids, io, T, m->w.tok_emb, m->w.tok_emb_scale, c.vocab,
+                    m->w.emb_norm, c.ln_eps, H, m->d_off, B, m->x, m->seg, s);
   }
   if (d_states) (void)hipMemcpyAsync(d_states, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
 
@@ -342,11 +342,91 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
   }
   if (n_run == c.n_layers && d_tok) {
     ProfScope ps(m, TTE_K_NORM, s);
-    launch_ln(m->x, m->w.final_norm, T, H, c.ln_eps, O_F32, d_tok, nullptr, s);
+    launch_ln(m->x, m->w.final_norm, T, H, c.ln_eps, O_F32, d_tok, nullptr, s, io);
   } else if (n_run == c.n_layers) {
     ProfScope ps(m, TTE_K_POOL, s);
-    launch_pool(m->x, m->w.final_norm, c.ln_eps, H, m->d_off, m->d_unit, B, n_units, m->partial, d_out, s);
+    launch_pool(m->x, m->w.final_norm, c.ln_eps, H, m->d_off, m->d_unit, B, n_units, m->partial, d_out, s, io);
   }
+}
+
+constexpr size_t MAX_GRAPHS = 64;
+
+// TTE_FLAG_GRAPH: the entry of a pack shape (inserted at its first call,
+// the least recently used one dropped beyond MAX_GRAPHS).
+tte_model::GraphEntry* graph_entry(tte_model* m, int kind, int T, int B, int units, bool* fresh) {
+  *fresh = false;
+  for (auto& g : m->graphs)
+    if (g.kind == kind && g.T == T && g.B == B && g.units == units) return &g;
+  if (m->graphs.size() >= MAX_GRAPHS) {
+    size_t lru = 0;
+    for (size_t i = 1; i < m->graphs.size(); ++i)
+      if (m->graphs[i].used < m->graphs[lru].used) lru = i;
+    if (m->graphs[lru].exec) {
+      // an earlier replay of it may still run on some stream
+      (void)hipDeviceSynchronize();
+      (void)hipGraphExecDestroy(m->graphs[lru].exec);
+    }
+    m->graphs.erase(m->graphs.begin() + lru);
+  }
+  m->graphs.push_back(tte_model::GraphEntry{kind, T, B, units, nullptr, false, ++m->graph_clock});
+  *fresh = true;
+  return &m->graphs.back();
+}
+
+// Validates and uploads a pack, then runs the pass: eagerly, or with
+// TTE_FLAG_GRAPH from the graph of the pack's shape (captured at the
+// shape's second call).
+tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t* h_off, int32_t B, float* d_out,
+                    float* d_states, int32_t n_dump, void* stream, float* d_tok = nullptr) {
+  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+  const tte_config& c = m->cfg;
+  tte_status st = check_pack(c, T, h_off, B);
+  if (st != TTE_OK) return st;
+  if (B == 0) return TTE_OK;
+  if (!d_ids) return fail(TTE_E_INVALID, "d_token_ids is NULL");
+  if (d_states) {
+    if (n_dump < 0 || n_dump > c.n_layers) return fail(TTE_E_INVALID, "n_dump must be in [0, n_layers]");
+  } else {
+    n_dump = -1;
+  }
+  const int n_run = (d_states && n_dump < c.n_layers) ? n_dump : c.n_layers;
+  if (n_run == c.n_layers && !d_out && !d_tok) return fail(TTE_E_INVALID, "d_out is NULL");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = hip_check(hipSetDevice(m->device), "hipSetDevice");
+  if (st != TTE_OK) return st;
+  (void)hipGetLastError();
+  const bool graph = (c.flags & TTE_FLAG_GRAPH) && !d_states && s != nullptr && !m->prof_on;
+  int n_units = 0;
+  st = upload_pack(m, h_off, B, &n_units, s, graph ? d_ids : nullptr, graph ? (d_tok ? d_tok : d_out) : nullptr);
+  if (st != TTE_OK) return st;
+  const PackIO* io = graph ? m->d_io : nullptr;
+  if (graph) {
+    bool fresh = false;
+    tte_model::GraphEntry* e = graph_entry(m, d_tok ? 1 : 0, T, B, n_units, &fresh);
+    e->used = ++m->graph_clock;
+    if (!fresh && !e->exec && !e->failed) {
+      // second call of this shape: record the sequence (nothing runs while
+      // the stream captures) and instantiate it
+      hipGraph_t g = nullptr;
+      hipError_t err = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+      if (err == hipSuccess) {
+        enqueue_pass(m, nullptr, io, T, B, n_units, nullptr, nullptr, n_run, d_tok ? d_tok : nullptr, s);
+        err = hipStreamEndCapture(s, &g);
+        if (err == hipSuccess) err = hipGraphInstantiate(&e->exec, g, nullptr, nullptr, 0);
+        if (g) (void)hipGraphDestroy(g);
+      }
+      (void)hipGetLastError();
+      if (err != hipSuccess) {
+        e->exec = nullptr;
+        e->failed = true;  // this shape runs eagerly from now on
+      }
+    }
+    if (e->exec) {
+      ++m->graph_replays;
+      return hip_check(hipGraphLaunch(e->exec, s), "hipGraphLaunch");
+    }
+  }
+  enqueue_pass(m, d_ids, io, T, B, n_units, d_out, d_states, n_run, d_tok, s);
   return hip_check(hipGetLastError(), "kernel launch");
 }
 
@@ -416,8 +496,9 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   m->y = b + L.y;
   m->kpart = reinterpret_cast<float*>(b + L.kpart);
   m->seg = reinterpret_cast<Seg*>(b + L.seg);
-  m->d_off = reinterpret_cast<int*>(b + L.off);
-  m->d_unit = reinterpret_cast<int*>(b + L.unit);
+  m->d_io = reinterpret_cast<PackIO*>(b + L.off);
+  m->d_off = reinterpret_cast<int*>(b + L.off + sizeof(PackIO));
+  m->d_unit = m->d_off + 1;
   m->partial = reinterpret_cast<float*>(b + L.partial);
   m->cosg = reinterpret_cast<const float*>(b + L.cosg);
   m->sing = reinterpret_cast<const float*>(b + L.sing);
@@ -445,8 +526,7 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   if (st == TTE_OK)
     st = hip_check(hipMemset(m->vt, 0, (size_t)c.hidden * L.vt_stride * act_bytes(c.precision)), "hipMemset(vt)");
   if (st == TTE_OK)
-    st = hip_check(hipHostMalloc((void**)&m->h_stage, sizeof(int) * 2 * ((size_t)c.max_texts + 1) * STAGE_SLOTS,
-                                 hipHostMallocDefault),
+    st = hip_check(hipHostMalloc((void**)&m->h_stage, sizeof(int) * stage_ints(c) * STAGE_SLOTS, hipHostMallocDefault),
                    "hipHostMalloc");
   int n_ev = 0;
   for (; st == TTE_OK && n_ev < STAGE_SLOTS; ++n_ev)
@@ -497,6 +577,15 @@ tte_status tte_destroy(tte_model* m) {
   }
   (void)hipHostFree(m->h_stage);
   for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
+  bool any_graph = false;
+  for (auto& g : m->graphs) any_graph |= g.exec != nullptr;
+  if (any_graph) {
+    // replays may still be running on the caller's streams
+    (void)hipSetDevice(m->device);
+    (void)hipDeviceSynchronize();
+    for (auto& g : m->graphs)
+      if (g.exec) (void)hipGraphExecDestroy(g.exec);
+  }
   delete m;
   return TTE_OK;
 }
@@ -658,6 +747,16 @@ tte_status tte_profile_start(tte_model* m, uint32_t class_mask, int32_t max_laun
   m->ev_overflow = false;
   m->prof_mask = class_mask;
   m->prof_on = true;
+  return TTE_OK;
+}
+
+tte_status tte_graph_stats(const tte_model* m, int32_t* n_shapes, int32_t* n_graphs, int64_t* n_replays) {
+  if (!m || !n_shapes || !n_graphs || !n_replays) return fail(TTE_E_INVALID, "NULL argument");
+  *n_shapes = (int32_t)m->graphs.size();
+  int32_t g = 0;
+  for (const auto& e : m->graphs) g += e.exec != nullptr;
+  *n_graphs = g;
+  *n_replays = m->graph_replays;
   return TTE_OK;
 }
 
