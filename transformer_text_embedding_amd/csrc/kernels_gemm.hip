@@ -52,6 +52,10 @@
 #include "common.h"
 #include "kernels.h"
 
+#ifndef TTE_BF16_PIPE
+#define TTE_BF16_PIPE 1
+#endif
+
 namespace tte {
 
 namespace {
@@ -122,6 +126,25 @@ __device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* const*
   if constexpr (PREC == P_I8 || PREC == P_I4) {
     if (lane < 32) dma16(s_src + kt * 4, stage + scale_at + wid * 512);
   }
+}
+
+// Instruction order for the scheduler over the preceding MFMAs (NM) and
+// LDS reads (NR): with MFMA_FIRST one MFMA leads (its operands were read
+// earlier), then read / MFMA pairs, then what is left of either; so the
+// reads of the next k-step issue between this k-step's MFMAs instead of
+// being hoisted ahead of them (which makes the MFMAs wait for every read).
+template <int NM, int NR, bool MFMA_FIRST>
+__device__ __forceinline__ void interleave() {
+  constexpr int lead = MFMA_FIRST ? 1 : 0;
+  constexpr int pairs = NR < NM - lead ? NR : NM - lead;
+  if constexpr (lead) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+#pragma unroll
+  for (int i = 0; i < pairs; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+  }
+  if constexpr (NR > pairs) __builtin_amdgcn_sched_group_barrier(0x100, NR - pairs, 0);
+  if constexpr (NM - lead - pairs > 0) __builtin_amdgcn_sched_group_barrier(0x008, NM - lead - pairs, 0);
 }
 
 // 8 packed 4-bit codes (4 bytes, the even input in the low nibble) as 8
@@ -218,10 +241,81 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
 #pragma unroll
     for (int b = 0; b < WN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  const int swz = KT == 256 ? li : KT == 128 ? (li & 7) : (((li >> 1) ^ (li >> 3)) & 3);
+#if TTE_BF16_PIPE
+  // (two-stage rings only: with a third stage the later load issue of this
+  // scheme measured slower for the long-K down-projection)
+  if constexpr (PREC == P_BF16 && G::STAGES == 2) {
+    // Fragment reads one 32-wide k-step ahead of the MFMAs, across the
+    // barrier: the last k-step's MFMAs of tile kt run while the first
+    // k-step's fragments of tile kt+1 come from LDS.  The barrier sits
+    // after the wave's last fragment read of tile kt has returned, so the
+    // stage of tile kt itself is free there and tile kt + STAGES goes into
+    // it: the ring holds STAGES tiles in flight (the prologue issues
+    // STAGES).
+    constexpr int KS = KT / 64;  // 32-element k-steps per tile
+    static_assert(KS % 2 == 0, "each tile starts in fragment set 0");
+    const int issued0 = min(G::STAGES, nk);
+    for (int p = 0; p < issued0; ++p)
+      issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, src, step, s_src, p, wid, lane, G::AREG + G::WREG);
+    wait_vm((issued0 - 1) * G::PER_TILE);  // tile 0 has landed (own loads)
+    __builtin_amdgcn_s_barrier();          // ... and every wave's
+    asm volatile("" ::: "memory");
+    bf16x8 fa[2][WM], fb[2][WN];
+    auto read_frags = [&](int stg, int ks, bf16x8* a, bf16x8* b) {
+      const uint8_t* st = smem + stg * G::TILE;
+      const uint8_t* As = st + (wm * 16 * WM + li) * ROW;
+      const uint8_t* Bs = st + G::AREG + (wn * 16 * WN + li) * G::WROW;
+      const int off = ((4 * ks + g) ^ swz) << 4;
+#pragma unroll
+      for (int t = 0; t < WM; ++t) a[t] = *reinterpret_cast<const bf16x8*>(As + t * 16 * ROW + off);
+#pragma unroll
+      for (int t = 0; t < WN; ++t) b[t] = *reinterpret_cast<const bf16x8*>(Bs + t * 16 * ROW + off);
+    };
+    auto mfma = [&](const bf16x8* a, const bf16x8* b) {
+#pragma unroll
+      for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < WN; ++nt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[mt], b[nt], acc[mt][nt], 0, 0, 0);
+    };
+    read_frags(0, 0, fa[0], fb[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int stg = kt % G::STAGES;
+      // k-steps 0 .. KS-2: the next k-step's fragments are read behind
+      // this one's MFMAs (sets alternate; KS is even, so a tile starts in
+      // set 0 and its last k-step is in set 1)
+#pragma unroll
+      for (int ks = 0; ks + 1 < KS; ++ks) {
+        mfma(fa[ks & 1], fb[ks & 1]);
+        read_frags(stg, ks + 1, fa[(ks + 1) & 1], fb[(ks + 1) & 1]);
+        interleave<WM * WN, WM + WN, true>();
+      }
+      // every fragment of tile kt has returned
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      if (kt + 1 < nk) {
+        // tile kt + 1 has landed; past the barrier no wave reads stage stg,
+        // so tile kt + STAGES goes there
+        wait_vm(min(G::STAGES - 2, nk - 2 - kt) * G::PER_TILE);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        if (kt + G::STAGES < nk)
+          issue_tile<G::QW, PREC, KT>(smem + stg * G::TILE, src, step, s_src, kt + G::STAGES, wid, lane,
+                                      G::AREG + G::WREG);
+      }
+      // k-step 0 of tile kt + 1 is read behind the last k-step's MFMAs of
+      // tile kt (after the last tile the read is of a stage no load writes
+      // any more, and unused)
+      read_frags((kt + 1) % G::STAGES, 0, fa[0], fb[0]);
+      mfma(fa[1], fb[1]);
+      interleave<WM * WN, WM + WN, false>();
+    }
+  } else
+#endif
+  {
   for (int p = 0; p < G::STAGES - 1 && p < nk; ++p)
     issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, src, step, s_src, p, wid, lane, G::AREG + G::WREG);
 
-  const int swz = KT == 256 ? li : KT == 128 ? (li & 7) : (((li >> 1) ^ (li >> 3)) & 3);
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of tile kt are done once at most `ahead` tiles of
     // its own loads remain in flight; the barrier publishes every wave's
@@ -323,6 +417,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
           }
       }
     }
+  }
+
   }
 
   // epilogue: lane holds rows 4g + r of column li in every 16 x 16 tile
@@ -532,17 +628,22 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
 //  * T256: 256 x 256, 8 waves of 128 x 64 (one block per CU): wide products
 //    with >= 512 such tiles, and the residual products of >= 8k rows;
 //  * T128W8 / T192W8: 128 x 128 or 192 x 128, 8 waves of 32 x 64 or
-//    48 x 64 (two blocks per CU): the other wide products (QKV always,
-//    GeGLU below the T256 size).  The height is the one with the smaller
-//    ceil(tiles / 256) * rows, a count of tile-rows the busiest CU works
-//    through (ties to 192: fewer tiles re-read A less): at 1.9k rows GeGLU
-//    runs 803 against 739 TFLOP/s in 192-row tiles, at 2048 rows 651
-//    against 771;
-//  * the 4-wave tiles for the 768-wide residual products: 32 x 128 when
-//    there are few tiles and K is short, else 64 x 128, with a third stage
-//    for long K (256-byte K tiles measured faster for the down-projection
-//    alone, 351 against 324 TFLOP/s at 1.9k rows, but slower inside the
-//    pass, 33.4 against 29.1 us per launch, and are not dispatched);
+//    48 x 64 (two blocks per CU): every other product (QKV always, GeGLU
+//    below the T256 size, the residual products below 8k rows).  The
+//    height is the one with the smaller ceil(tiles / 256) * rows, a count
+//    of tile-rows the busiest CU works through (ties to 192: fewer tiles
+//    re-read A less): at 1.9k rows GeGLU runs 803 against 739 TFLOP/s in
+//    192-row tiles, at 2048 rows 651 against 771.  For the 768-wide
+//    residual products of a ~2k-token pack this leaves most CUs idle when
+//    one pack runs alone (90 tiles; 64 x 128 4-wave tiles finish a lone
+//    down-projection faster, 30 against 37 us), but packs on concurrent
+//    streams fill those CUs and the larger tiles load less per flop: the
+//    4-stream pass runs 1.40M against 1.32M tokens/s;
+//  * the 4-wave tiles for the 768-wide residual products in fp32, int8 and
+//    4-bit (larger tiles measured no faster there: their GEMMs are bound by
+//    the VALU block-scale work or the fp32 rate): 32 x 128 when there are
+//    few tiles and K is short, else 64 x 128, with a third stage for long
+//    K;
 //  * int8 (its scale staging feeds 32 W rows per wave) and fp32 (measured
 //    slower with 8 waves: GeGLU at 957 tokens 54% against 64% of the fp32
 //    peak) keep 4-wave tiles: 128 x 128 once there are >= 1024 such tiles.
@@ -553,10 +654,8 @@ TileCfg pick_tiles(int prec, int epi, int M, int n_cols, int K) {
   const long tiles256 = (long)((M + 255) / 256) * (n_cols / 256);
   if (prec != P_BF16) {
     if (tiles128 >= 1024) return T128;
-  } else if (epi == E_RESID) {
-    if (M >= 8192 && n_cols % 256 == 0) return T256;
   } else {
-    if (tiles256 >= 512 && n_cols % 256 == 0) return T256;
+    if (epi == E_RESID ? (M >= 8192 && n_cols % 256 == 0) : (tiles256 >= 512 && n_cols % 256 == 0)) return T256;
     const long c128 = ((tiles128 + 255) / 256) * 128;
     const long c192 = (((long)((M + 191) / 192) * (n_cols / 128) + 255) / 256) * 192;
     return c192 <= c128 ? T192W8 : T128W8;
