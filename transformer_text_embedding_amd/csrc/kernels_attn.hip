@@ -230,15 +230,13 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
         }
       }
     } else {
+      // P to bf16 with the pack-convert instruction (round to nearest even,
+      // as f32_to_bf16 for the finite values here)
       bf16x8 pb[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        u16x8 tt;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          tt[e] = f32_to_bf16(sv[(2 * u) * 4 + e]);
-          tt[4 + e] = f32_to_bf16(sv[(2 * u + 1) * 4 + e]);
-        }
+        const u32x4 tt = {pack_bf16x2(sv[8 * u + 0], sv[8 * u + 1]), pack_bf16x2(sv[8 * u + 2], sv[8 * u + 3]),
+                          pack_bf16x2(sv[8 * u + 4], sv[8 * u + 5]), pack_bf16x2(sv[8 * u + 6], sv[8 * u + 7])};
         pb[u] = __builtin_bit_cast(bf16x8, tt);
       }
 #pragma unroll
@@ -268,9 +266,9 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
     uint16_t* op = reinterpret_cast<uint16_t*>(out) + (size_t)qi * H + h * 64;
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt) {
-      const u16x4 tt = {f32_to_bf16(oacc[dt][0] * inv_l), f32_to_bf16(oacc[dt][1] * inv_l),
-                        f32_to_bf16(oacc[dt][2] * inv_l), f32_to_bf16(oacc[dt][3] * inv_l)};
-      *reinterpret_cast<u16x4*>(op + 16 * dt + 4 * g) = tt;
+      const uint32_t lo = pack_bf16x2(oacc[dt][0] * inv_l, oacc[dt][1] * inv_l);
+      const uint32_t hi = pack_bf16x2(oacc[dt][2] * inv_l, oacc[dt][3] * inv_l);
+      *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) = make_uint2(lo, hi);
     }
   }
 }

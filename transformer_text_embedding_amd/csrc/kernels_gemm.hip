@@ -36,10 +36,11 @@
 //         a_scale[m] multiplies once in the epilogue.
 //   int4 (weights; activations int8): W rows are 64 bytes of packed codes
 //         per 128-input K tile and unpack to int8 in registers before the
-//         same MFMA; a second MFMA against all-ones gives the activations'
-//         block sum S, and acc += float(P) * es - float(S) * eo with the
-//         block's scale and offset decoded from the 16-byte record that
-//         rides the LDS ring where the int8 scales do.
+//         same MFMA, and acc += float(P) * es per block; a transposed MFMA
+//         against all-ones gives the activations' block sums S, and the
+//         tile's offset term sum_b S * (-eo) is one fp32 MFMA; the block
+//         scales and offsets come from the 16-byte record that rides the
+//         LDS ring where the int8 scales do.
 //
 // Epilogues: STORE (fp32 or bf16), RESID (fp32 C += result), GEGLU.  For
 // GEGLU the W tile rows are chosen so that the first half of every wave's
@@ -369,6 +370,13 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
       for (int nt = 0; nt < WN; ++nt) rw[nt] = *reinterpret_cast<const u32x4*>(rec + 16 * 16 * nt);
       const int swz4 = ((li >> 1) ^ (li >> 3)) & 3;  // the W rows' 64-byte swizzle (row & 15 = li)
       const long ones = 0x0101010101010101l;
+      // s_blk[mt]: the activations' block sum S[row li][block g] of this
+      // lane; the all-ones product taken transposed (ones x A^T) leaves
+      // S[row li][block c] in every register of the lanes of column li, and
+      // the lanes of k-group g keep block c = g
+      int s_blk[WM];
+#pragma unroll
+      for (int mt = 0; mt < WM; ++mt) s_blk[mt] = 0;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const int off = (((2 * c + (g >> 1)) ^ swz) << 4) + ((g & 1) << 3);
@@ -380,19 +388,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
           bf[t] = unpack_q4(*reinterpret_cast<const uint32_t*>(Bs + t * 16 * G::WROW + ((c ^ swz4) << 4) + 4 * g));
 #pragma unroll
         for (int mt = 0; mt < WM; ++mt) {
-          // S: the activations' block sum, the same in every column
-          const i32x4 sum = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[mt], ones, i32x4{0, 0, 0, 0}, 0, 0, 0);
+          const i32x4 st = __builtin_amdgcn_mfma_i32_16x16x32_i8(ones, af[mt], i32x4{0, 0, 0, 0}, 0, 0, 0);
+          s_blk[mt] = g == c ? st[0] : s_blk[mt];
 #pragma unroll
           for (int nt = 0; nt < WN; ++nt) {
-            const float d = __uint_as_float(rw[nt][2]), dmin = __uint_as_float(rw[nt][3]);
-            const float es = d * (float)((rw[nt][0] >> (8 * c)) & 0xFF);
-            const float eo = dmin * (float)((rw[nt][1] >> (8 * c)) & 0xFF);
+            const float es = __uint_as_float(rw[nt][2]) * (float)((rw[nt][0] >> (8 * c)) & 0xFF);
             const i32x4 p = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[mt], bf[nt], i32x4{0, 0, 0, 0}, 0, 0, 0);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-              acc[mt][nt][r] = __builtin_fmaf(-(float)sum[r], eo, __builtin_fmaf((float)p[r], es, acc[mt][nt][r]));
+            for (int r = 0; r < 4; ++r) acc[mt][nt][r] = __builtin_fmaf((float)p[r], es, acc[mt][nt][r]);
           }
         }
+      }
+      // the offsets of the tile's 4 blocks as one fp32 product:
+      // acc[m][n] += sum_b S[m][b] * (-eo[n][b]), with lane (row / column
+      // li, block g) holding S[li][g] and -eo[li][g] = -dmin * mn[g]
+#pragma unroll
+      for (int nt = 0; nt < WN; ++nt) {
+        const float neg_eo = -(__uint_as_float(rw[nt][3]) * (float)((rw[nt][1] >> (8 * g)) & 0xFF));
+#pragma unroll
+        for (int mt = 0; mt < WM; ++mt)
+          acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32((float)s_blk[mt], neg_eo, acc[mt][nt], 0, 0, 0);
       }
     } else {
       const float* sc = reinterpret_cast<const float*>(stage + G::AREG + G::WREG);
