@@ -80,3 +80,35 @@ def test_graph_replay_full(name):
     w = ti.cached_storage_weights(cfg)
     shapes = [list(np.diff(p.offsets)) for p in ti.make_packs(name)[:2]]
     _check_replays(cfg, w, shapes, max_tokens=2048, rounds=2)
+
+
+def test_graph_table_drops_least_recently_used():
+    """More pack shapes than the table keeps (64): the least recently used
+    are dropped, captured graphs among them released after a device
+    synchronisation, and a dropped shape starts over (eager, then captured);
+    every call still matches the eager pass."""
+    t = torch()
+    cfg = ti.workload("tiny_fp32")["cfg"]
+    w = ti.storage_weights(cfg, ti.make_fp32_weights(cfg))
+    eager = Model(cfg, w, max_tokens=512, max_text_len=512, max_texts=64)
+    graph = Model(cfg, None, max_tokens=512, max_text_len=512, max_texts=64, shared_from=eager, graph=True)
+    try:
+        rng = np.random.default_rng(11)
+        packs = [ti.random_pack(rng, [3 + i, 5], cfg.vocab) for i in range(70)]  # 70 distinct shapes
+        ref = [host(eager.embed_pack(dev(p.ids), p.offsets)) for p in packs]
+        s = t.cuda.Stream()
+        order = list(range(10)) * 2 + list(range(10, 70)) + [0, 0]
+        outs = []
+        with t.cuda.stream(s):
+            for i in order:
+                outs.append((i, graph.embed_pack(dev(packs[i].ids), packs[i].offsets, stream=s)))
+        sync()
+        # shapes 0-9 captured at their second call (10 graphs); 60 new shapes
+        # drop shapes 0-5 with their graphs; shape 0 returns, drops shape 6,
+        # runs eagerly, and is captured again at its next call
+        assert B.tte_graph_stats(graph.handle) == (64, 4, 11), B.tte_graph_stats(graph.handle)
+        for n, (i, out) in enumerate(outs):
+            assert np.array_equal(host(out), ref[i]), f"call {n} (pack {i}) differs"
+    finally:
+        graph.close()
+        eager.close()
