@@ -27,9 +27,12 @@
 // the matrix-core output layout puts one query per lane column: each lane's
 // scores of its query are directly the B operand of the P*V product, and the
 // running max / sum / rescale of a query stay in the lanes that hold it.
-// Softmax uses exp2 with log2(e)/8 folded into one multiply.  fp32 variant:
-// v_mfma_f32_16x16x4_f32; bf16 variant: v_mfma_f32_16x16x32_bf16 with P
-// rounded to bf16 and all statistics in fp32.
+// Softmax uses exp2 with log2(e)/8 folded into one multiply; the output and
+// sum are rescaled only on tiles where some lane's running max moved.  fp32
+// variant: v_mfma_f32_16x16x4_f32; bf16 variant: v_mfma_f32_16x16x32_bf16
+// with P rounded to bf16, its per-query sum taken on the matrix cores too
+// (against an all-ones block, so numerator and denominator use the same
+// rounded P), and all statistics in fp32.
 #include "common.h"
 #include "kernels.h"
 
@@ -136,6 +139,9 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
 #pragma unroll
   for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = NEG_INF, l_run = 0.f;
+  // bf16: the running sum of P comes from the matrix cores (an all-ones
+  // block of V^T rows), every register of lacc holding the lane's query sum
+  f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
 
   for (int t = 0; t < C::STAGES - 1 && t < n_tiles; ++t) issue(t);
   for (int t = 0; t < n_tiles; ++t) {
@@ -200,21 +206,28 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
     mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
     const float m_new = fmaxf(m_run, mloc);
     const float m_use = m_new == NEG_INF ? 0.f : m_new;
-    // every exponent below is <= 0 (or -inf): the hardware exp2 suffices
-    const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
-    const float mb = m_use * scale_log2;
-    float psum = 0.f;
+    // the output and sum are rescaled only when some lane's running max
+    // moved (otherwise the factor is exactly 1)
+    if (__any(m_new != m_run)) {
+      // every exponent below is <= 0 (or -inf): the hardware exp2 suffices
+      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      sv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -mb));
-      psum += sv[i];
+      for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+      if constexpr (PREC == P_F32) l_run *= alpha;
+      else lacc *= alpha;
     }
-    psum += __shfl_xor(psum, 16, 64);
-    psum += __shfl_xor(psum, 32, 64);
-    l_run = l_run * alpha + psum;
     m_run = m_new;
+    const float mb = m_use * scale_log2;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
+    for (int i = 0; i < 16; ++i) sv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -mb));
+    if constexpr (PREC == P_F32) {
+      float psum = 0.f;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) psum += sv[i];
+      psum += __shfl_xor(psum, 16, 64);
+      psum += __shfl_xor(psum, 32, 64);
+      l_run += psum;
+    }
 
     // ---- O^T += V^T P^T ----
     if constexpr (PREC == P_F32) {
@@ -239,6 +252,10 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
                           pack_bf16x2(sv[8 * u + 4], sv[8 * u + 5]), pack_bf16x2(sv[8 * u + 6], sv[8 * u + 7])};
         pb[u] = __builtin_bit_cast(bf16x8, tt);
       }
+      // sum of the (bf16) P of each query: ones x P^T
+      const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+#pragma unroll
+      for (int u = 0; u < 2; ++u) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[u], lacc, 0, 0, 0);
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const uint8_t* vr = Vs + (16 * dt + li) * C::ROWB;
@@ -256,6 +273,7 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
   }
 
   if (!qvalid) return;
+  if constexpr (PREC == P_BF16) l_run = lacc[0];
   const float inv_l = 1.f / l_run;
   // lane holds dims 16 dt + 4 g + r of query qi
   if constexpr (PREC == P_F32) {
