@@ -14,11 +14,12 @@
 // simply start(q) <= key < end(q); no per-key lookup is needed.
 //
 // How: flash-style streaming over the packed token axis.  A block takes 64
-// consecutive queries (they may span several texts) and walks 64-key tiles
-// over the union of their allowed key ranges only (a local layer needs at
-// most 64 + 2*window keys, a global one the texts of its queries), so fully
-// masked tiles are never loaded; a wave also skips the matrix work of tiles
-// outside its own 16 queries' range.  K rows and V^T rows of a tile stream
+// consecutive queries (128 on bf16 global layers: 16 or 32 per wave; they
+// may span several texts) and walks 64-key tiles over the union of their
+// allowed key ranges only (a local layer needs at most 64 + 2*window keys, a
+// global one the texts of its queries), so fully masked tiles are never
+// loaded; a wave also skips the matrix work of tiles outside its own
+// queries' range.  K rows and V^T rows of a tile stream
 // global -> LDS with direct-to-LDS loads into a double buffer (the next
 // tile loads while the current one is used), rows XOR-swizzled by 16-byte
 // chunk so fragment reads are conflict-free.
@@ -40,7 +41,6 @@ namespace tte {
 
 namespace {
 
-constexpr int AQ = 64;   // queries per block
 constexpr int AKT = 64;  // keys per tile
 constexpr float NEG_INF = -__builtin_huge_valf();
 
@@ -56,58 +56,67 @@ struct AttnCfg {
   static constexpr int ALIGN = 16 / ES;               // key alignment of a V^T row segment
 };
 
-template <int PREC, int STAGES>
+template <int PREC, int STAGES, int NQ>
 __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const void* __restrict__ vt, int vt_stride,
                                               void* __restrict__ out, const Seg* __restrict__ seg, int T, int nh,
                                               int is_global, int window, float scale_log2) {
   using C = AttnCfg<PREC, STAGES>;
+  constexpr int QPW = 16 * NQ;  // queries per wave: NQ 16-query column tiles sharing each K / V^T fragment
+  constexpr int BQ = 4 * QPW;   // queries per block
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int H = nh * 64, ld = 3 * H;
   const int h = blockIdx.y;
-  const int i0 = blockIdx.x * AQ;
+  const int i0 = blockIdx.x * BQ;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
 
   // key range of the block (union over its queries) and of this wave
-  const int ilast = min(i0 + AQ - 1, T - 1);
+  const int ilast = min(i0 + BQ - 1, T - 1);
   const Seg sa = seg[i0], sb = seg[ilast];
   int kstart = sa.start, kend = sb.end;
   if (!is_global) {
     kstart = max(kstart, i0 - window);
     kend = min(kend, ilast + window + 1);
   }
-  const int wq_lo = min(i0 + 16 * w, T - 1), wq_hi = min(i0 + 16 * w + 15, T - 1);
+  const int wq0 = i0 + QPW * w;
+  const bool wave_any = wq0 < T;
+  const int wq_lo = min(wq0, T - 1), wq_hi = min(wq0 + QPW - 1, T - 1);
   const Seg swl = seg[wq_lo], swh = seg[wq_hi];
   int wk_lo = swl.start, wk_hi = swh.end;
   if (!is_global) {
     wk_lo = max(wk_lo, wq_lo - window);
     wk_hi = min(wk_hi, wq_hi + window + 1);
   }
-  const bool wave_any = i0 + 16 * w < T;
 
-  const int qi = i0 + 16 * w + li;
-  const bool qvalid = qi < T;
-  const int qrow = qvalid ? qi : T - 1;
-  const Seg qs = seg[qrow];
-  // keys this lane's query may see: [k_lo, k_lo + k_span) (its text, and on
-  // a local layer the window); an invalid query sees none
-  int k_lo = qs.start, k_hi = qs.end;
-  if (!is_global) {
-    k_lo = max(k_lo, qi - window);
-    k_hi = min(k_hi, qi + window + 1);
-  }
-  const unsigned k_span = qvalid ? (unsigned)(k_hi - k_lo) : 0u;
-
-  // ---- Q fragment (already rotated) ----
-  f32x4 qf[4];   // fp32: dims 16 kc + 4 g + e
-  bf16x8 qb[2];  // bf16: dims 32 kc + 8 g + e
-  if constexpr (PREC == P_F32) {
-    const float* qp = reinterpret_cast<const float*>(qk) + (size_t)qrow * ld + h * 64;
+  // this lane's query in each 16-query tile, and the keys it may see:
+  // [k_lo, k_lo + k_span) (its text, and on a local layer the window); an
+  // invalid query sees none
+  int qi[NQ], k_lo[NQ];
+  unsigned k_span[NQ];
+  f32x4 qf[NQ][4];   // fp32: dims 16 kc + 4 g + e
+  bf16x8 qb[NQ][2];  // bf16: dims 32 kc + 8 g + e
 #pragma unroll
-    for (int kc = 0; kc < 4; ++kc) qf[kc] = *reinterpret_cast<const f32x4*>(qp + 16 * kc + 4 * g);
-  } else {
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(qk) + (size_t)qrow * ld + h * 64;
+  for (int qt = 0; qt < NQ; ++qt) {
+    qi[qt] = wq0 + 16 * qt + li;
+    const bool valid = qi[qt] < T;
+    const int qrow = valid ? qi[qt] : T - 1;
+    const Seg qs = seg[qrow];
+    int lo = qs.start, hi = qs.end;
+    if (!is_global) {
+      lo = max(lo, qi[qt] - window);
+      hi = min(hi, qi[qt] + window + 1);
+    }
+    k_lo[qt] = lo;
+    k_span[qt] = valid ? (unsigned)(hi - lo) : 0u;
+    // Q fragment (already rotated)
+    if constexpr (PREC == P_F32) {
+      const float* qp = reinterpret_cast<const float*>(qk) + (size_t)qrow * ld + h * 64;
 #pragma unroll
-    for (int kc = 0; kc < 2; ++kc) qb[kc] = *reinterpret_cast<const bf16x8*>(qp + 32 * kc + 8 * g);
+      for (int kc = 0; kc < 4; ++kc) qf[qt][kc] = *reinterpret_cast<const f32x4*>(qp + 16 * kc + 4 * g);
+    } else {
+      const uint16_t* qp = reinterpret_cast<const uint16_t*>(qk) + (size_t)qrow * ld + h * 64;
+#pragma unroll
+      for (int kc = 0; kc < 2; ++kc) qb[qt][kc] = *reinterpret_cast<const bf16x8*>(qp + 32 * kc + 8 * g);
+    }
   }
 
   // ---- load plan: instruction j of wave w covers tile rows
@@ -135,13 +144,19 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
     }
   };
 
-  f32x4 oacc[4];
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) oacc[dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = NEG_INF, l_run = 0.f;
+  f32x4 oacc[NQ][4];
+  float m_run[NQ], l_run[NQ];
   // bf16: the running sum of P comes from the matrix cores (an all-ones
   // block of V^T rows), every register of lacc holding the lane's query sum
-  f32x4 lacc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 lacc[NQ];
+#pragma unroll
+  for (int qt = 0; qt < NQ; ++qt) {
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    m_run[qt] = NEG_INF;
+    l_run[qt] = 0.f;
+    lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
 
   for (int t = 0; t < C::STAGES - 1 && t < n_tiles; ++t) issue(t);
   for (int t = 0; t < n_tiles; ++t) {
@@ -156,80 +171,91 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
     const uint8_t* Ks = smem + (t % C::STAGES) * C::TILE;
     const uint8_t* Vs = Ks + 64 * C::ROWB;
 
-    // ---- S^T = K Q^T: lane holds keys 16 mt + 4 g + r of query li ----
-    f32x4 sacc[4];
+    // ---- S^T = K Q^T: lane holds keys 16 mt + 4 g + r of query li of
+    // each query tile; a K fragment serves all NQ query tiles ----
+    f32x4 sacc[NQ][4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) {
-      sacc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int qt = 0; qt < NQ; ++qt) sacc[qt][mt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const uint8_t* kr = Ks + (16 * mt + li) * C::ROWB;
       if constexpr (PREC == P_F32) {
 #pragma unroll
         for (int kc = 0; kc < 4; ++kc) {
           const f32x4 a = *reinterpret_cast<const f32x4*>(kr + (((4 * kc + g) ^ (li & 7)) << 4));
 #pragma unroll
-          for (int s = 0; s < 4; ++s) sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], qf[kc][s], sacc[mt], 0, 0, 0);
+          for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int qt = 0; qt < NQ; ++qt)
+              sacc[qt][mt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[s], qf[qt][kc][s], sacc[qt][mt], 0, 0, 0);
         }
       } else {
 #pragma unroll
         for (int kc = 0; kc < 2; ++kc) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(kr + (((4 * kc + g) ^ (li & 7)) << 4));
-          sacc[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[kc], sacc[mt], 0, 0, 0);
+#pragma unroll
+          for (int qt = 0; qt < NQ; ++qt)
+            sacc[qt][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qb[qt][kc], sacc[qt][mt], 0, 0, 0);
         }
       }
     }
 
-    // ---- mask, online softmax.  The lane holds keys j0 + 16 mt + 4 g + r
-    // of its query; key kj is allowed iff kj - k_lo < k_span (unsigned).  A
-    // tile whose keys every lane of the wave may all see skips the test ----
-    float sv[16];
-    float mloc = NEG_INF;
-    const int kb = j0 + 4 * g - k_lo;  // key offset of element (0, 0) from k_lo
-    if (__all((unsigned)kb < k_span && (unsigned)(kb + 51) < k_span)) {
+    // ---- mask, online softmax, per query tile.  The lane holds keys
+    // j0 + 16 mt + 4 g + r of its query; key kj is allowed iff
+    // kj - k_lo < k_span (unsigned).  A tile whose keys every lane of the
+    // wave may all see skips the test ----
+    float sv[NQ][16];
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+    for (int qt = 0; qt < NQ; ++qt) {
+      float mloc = NEG_INF;
+      const int kb = j0 + 4 * g - k_lo[qt];  // key offset of element (0, 0) from k_lo
+      if (__all((unsigned)kb < k_span[qt] && (unsigned)(kb + 51) < k_span[qt])) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          sv[mt * 4 + r] = sacc[mt][r];
-          mloc = fmaxf(mloc, sv[mt * 4 + r]);
-        }
-    } else {
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt)
+          for (int r = 0; r < 4; ++r) {
+            sv[qt][mt * 4 + r] = sacc[qt][mt][r];
+            mloc = fmaxf(mloc, sv[qt][mt * 4 + r]);
+          }
+      } else {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const bool ok = (unsigned)(kb + 16 * mt + r) < k_span;
-          sv[mt * 4 + r] = ok ? sacc[mt][r] : NEG_INF;
-          mloc = fmaxf(mloc, sv[mt * 4 + r]);
-        }
-    }
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-    mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
-    const float m_new = fmaxf(m_run, mloc);
-    const float m_use = m_new == NEG_INF ? 0.f : m_new;
-    // the output and sum are rescaled only when some lane's running max
-    // moved (otherwise the factor is exactly 1)
-    if (__any(m_new != m_run)) {
-      // every exponent below is <= 0 (or -inf): the hardware exp2 suffices
-      const float alpha = __builtin_amdgcn_exp2f((m_run - m_use) * scale_log2);
+        for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-      for (int dt = 0; dt < 4; ++dt) oacc[dt] *= alpha;
-      if constexpr (PREC == P_F32) l_run *= alpha;
-      else lacc *= alpha;
-    }
-    m_run = m_new;
-    const float mb = m_use * scale_log2;
+          for (int r = 0; r < 4; ++r) {
+            const bool ok = (unsigned)(kb + 16 * mt + r) < k_span[qt];
+            sv[qt][mt * 4 + r] = ok ? sacc[qt][mt][r] : NEG_INF;
+            mloc = fmaxf(mloc, sv[qt][mt * 4 + r]);
+          }
+      }
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
+      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      const float m_new = fmaxf(m_run[qt], mloc);
+      const float m_use = m_new == NEG_INF ? 0.f : m_new;
+      // the output and sum are rescaled only when some lane's running max
+      // moved (otherwise the factor is exactly 1)
+      if (__any(m_new != m_run[qt])) {
+        // every exponent below is <= 0 (or -inf): the hardware exp2 suffices
+        const float alpha = __builtin_amdgcn_exp2f((m_run[qt] - m_use) * scale_log2);
 #pragma unroll
-    for (int i = 0; i < 16; ++i) sv[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[i], scale_log2, -mb));
-    if constexpr (PREC == P_F32) {
-      float psum = 0.f;
+        for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] *= alpha;
+        if constexpr (PREC == P_F32) l_run[qt] *= alpha;
+        else lacc[qt] *= alpha;
+      }
+      m_run[qt] = m_new;
+      const float mb = m_use * scale_log2;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) psum += sv[i];
-      psum += __shfl_xor(psum, 16, 64);
-      psum += __shfl_xor(psum, 32, 64);
-      l_run += psum;
+      for (int i = 0; i < 16; ++i) sv[qt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[qt][i], scale_log2, -mb));
+      if constexpr (PREC == P_F32) {
+        float psum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) psum += sv[qt][i];
+        psum += __shfl_xor(psum, 16, 64);
+        psum += __shfl_xor(psum, 32, 64);
+        l_run[qt] += psum;
+      }
     }
 
-    // ---- O^T += V^T P^T ----
+    // ---- O^T += V^T P^T; a V^T fragment serves all NQ query tiles ----
     if constexpr (PREC == P_F32) {
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
@@ -239,23 +265,29 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
           const f32x4 a = *reinterpret_cast<const f32x4*>(vr + (((4 * mt + g) ^ (li & 7)) << 4));
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], sv[mt * 4 + r], oacc[dt], 0, 0, 0);
+#pragma unroll
+            for (int qt = 0; qt < NQ; ++qt)
+              oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[r], sv[qt][mt * 4 + r], oacc[qt][dt], 0, 0, 0);
         }
       }
     } else {
       // P to bf16 with the pack-convert instruction (round to nearest even,
       // as f32_to_bf16 for the finite values here)
-      bf16x8 pb[2];
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const u32x4 tt = {pack_bf16x2(sv[8 * u + 0], sv[8 * u + 1]), pack_bf16x2(sv[8 * u + 2], sv[8 * u + 3]),
-                          pack_bf16x2(sv[8 * u + 4], sv[8 * u + 5]), pack_bf16x2(sv[8 * u + 6], sv[8 * u + 7])};
-        pb[u] = __builtin_bit_cast(bf16x8, tt);
-      }
-      // sum of the (bf16) P of each query: ones x P^T
+      bf16x8 pb[NQ][2];
       const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
 #pragma unroll
-      for (int u = 0; u < 2; ++u) lacc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[u], lacc, 0, 0, 0);
+      for (int qt = 0; qt < NQ; ++qt) {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          const u32x4 tt = {pack_bf16x2(sv[qt][8 * u + 0], sv[qt][8 * u + 1]),
+                            pack_bf16x2(sv[qt][8 * u + 2], sv[qt][8 * u + 3]),
+                            pack_bf16x2(sv[qt][8 * u + 4], sv[qt][8 * u + 5]),
+                            pack_bf16x2(sv[qt][8 * u + 6], sv[qt][8 * u + 7])};
+          pb[qt][u] = __builtin_bit_cast(bf16x8, tt);
+          // sum of the (bf16) P of each query: ones x P^T
+          lacc[qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ones, pb[qt][u], lacc[qt], 0, 0, 0);
+        }
+      }
 #pragma unroll
       for (int dt = 0; dt < 4; ++dt) {
         const uint8_t* vr = Vs + (16 * dt + li) * C::ROWB;
@@ -265,28 +297,32 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
           const u16x4 lo = *reinterpret_cast<const u16x4*>(vr + (((4 * u + (g >> 1)) ^ (li & 7)) << 4) + ((g & 1) << 3));
           const u16x4 hi =
               *reinterpret_cast<const u16x4*>(vr + (((4 * u + 2 + (g >> 1)) ^ (li & 7)) << 4) + ((g & 1) << 3));
-          const u16x8 tt = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          oacc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, tt), pb[u], oacc[dt], 0, 0, 0);
+          const bf16x8 a = __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+#pragma unroll
+          for (int qt = 0; qt < NQ; ++qt)
+            oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qt][u], oacc[qt][dt], 0, 0, 0);
         }
       }
     }
   }
 
-  if (!qvalid) return;
-  if constexpr (PREC == P_BF16) l_run = lacc[0];
-  const float inv_l = 1.f / l_run;
-  // lane holds dims 16 dt + 4 g + r of query qi
-  if constexpr (PREC == P_F32) {
-    float* op = reinterpret_cast<float*>(out) + (size_t)qi * H + h * 64;
+  // lane holds dims 16 dt + 4 g + r of query qi of each query tile
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g) = oacc[dt] * inv_l;
-  } else {
-    uint16_t* op = reinterpret_cast<uint16_t*>(out) + (size_t)qi * H + h * 64;
+  for (int qt = 0; qt < NQ; ++qt) {
+    if (qi[qt] >= T) continue;
+    const float inv_l = 1.f / (PREC == P_BF16 ? lacc[qt][0] : l_run[qt]);
+    if constexpr (PREC == P_F32) {
+      float* op = reinterpret_cast<float*>(out) + (size_t)qi[qt] * H + h * 64;
 #pragma unroll
-    for (int dt = 0; dt < 4; ++dt) {
-      const uint32_t lo = pack_bf16x2(oacc[dt][0] * inv_l, oacc[dt][1] * inv_l);
-      const uint32_t hi = pack_bf16x2(oacc[dt][2] * inv_l, oacc[dt][3] * inv_l);
-      *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) = make_uint2(lo, hi);
+      for (int dt = 0; dt < 4; ++dt) *reinterpret_cast<f32x4*>(op + 16 * dt + 4 * g) = oacc[qt][dt] * inv_l;
+    } else {
+      uint16_t* op = reinterpret_cast<uint16_t*>(out) + (size_t)qi[qt] * H + h * 64;
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt) {
+        const uint32_t lo = pack_bf16x2(oacc[qt][dt][0] * inv_l, oacc[qt][dt][1] * inv_l);
+        const uint32_t hi = pack_bf16x2(oacc[qt][dt][2] * inv_l, oacc[qt][dt][3] * inv_l);
+        *reinterpret_cast<uint2*>(op + 16 * dt + 4 * g) = make_uint2(lo, hi);
+      }
     }
   }
 }
@@ -330,24 +366,38 @@ __global__ __launch_bounds__(256) void k_qkv_prep(const void* __restrict__ in, v
 void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, void* o, const Seg* seg, int T,
                       int n_heads, int is_global, int window, hipStream_t s) {
   if (T <= 0) return;
-  const dim3 grid((T + AQ - 1) / AQ, n_heads);
   const float scale_log2 = 0.125f * 1.4426950408889634f;
   // a double buffer: deeper rings (3 or 4 stages) measured slower on MI355X
   constexpr int ST = 2;
   static bool attr_set = false;  // dynamic LDS above 64 KB must be allowed once
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_BF16, ST>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_BF16, ST, 1>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, AttnCfg<P_BF16, ST>::LDS);
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_F32, ST>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_BF16, ST, 2>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, AttnCfg<P_BF16, ST>::LDS);
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_F32, ST, 1>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, AttnCfg<P_F32, ST>::LDS);
     attr_set = true;
   }
-  if (prec == P_BF16)
-    k_attn<P_BF16, ST><<<grid, 256, AttnCfg<P_BF16, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global,
+  if (prec == P_BF16) {
+    // global layers: 32 queries per wave (128 per block), each K / V^T
+    // fragment feeding two query tiles (4x4096 texts: 4.22 -> 4.10 ms per
+    // pass); local layers keep 16 (their 128-query blocks span more keys:
+    // 0.58 -> 0.70 ms)
+    if (is_global) {
+      const dim3 grid((T + 127) / 128, n_heads);
+      k_attn<P_BF16, ST, 2><<<grid, 256, AttnCfg<P_BF16, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads,
+                                                                        is_global, window, scale_log2);
+    } else {
+      const dim3 grid((T + 63) / 64, n_heads);
+      k_attn<P_BF16, ST, 1><<<grid, 256, AttnCfg<P_BF16, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads,
+                                                                        is_global, window, scale_log2);
+    }
+  } else {
+    const dim3 grid((T + 63) / 64, n_heads);
+    k_attn<P_F32, ST, 1><<<grid, 256, AttnCfg<P_F32, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global,
                                                                   window, scale_log2);
-  else
-    k_attn<P_F32, ST><<<grid, 256, AttnCfg<P_F32, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global,
-                                                                window, scale_log2);
+  }
 }
 
 void launch_qkv_prep(int prec, const void* qkv_in, void* qk_out, const QkvOut& qo, int T, hipStream_t s) {
