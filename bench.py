@@ -126,6 +126,8 @@ def main():
                     help="pooled unit vectors per text (tte_embed) or per-token states (tte_embed_tokens)")
     ap.add_argument("--split-k", action="store_true",
                     help="TTE_FLAG_SPLIT_K: split the down-projection of short packs (lower single-call latency)")
+    ap.add_argument("--merged", action="store_true",
+                    help="secondary number: all packs of a step concatenated into one call on one stream")
     ap.add_argument("--graph", action="store_true",
                     help="TTE_FLAG_GRAPH: replay each pack's captured HIP graph (needs --warmup >= 2)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=3000)
@@ -172,13 +174,20 @@ def main():
     t0 = time.perf_counter()
     w = ti.cached_storage_weights(cfg)
     packs = ti.make_packs(a.workload)
+    cpu_packs = packs  # the CPU baseline always takes the workload's own packs
+    if a.merged:
+        # texts are independent: the whole step as one pack (one call)
+        packs = [ti.pack_from_texts([p.text(b) for p in packs for b in range(p.n_texts)])]
+        a.streams = 1
     log(f"inputs ready in {time.perf_counter() - t0:.1f}s: {len(packs)} packs, "
         f"{sum(p.n_tokens for p in packs)} tokens")
     max_tokens = max(p.n_tokens for p in packs)
     S = max(1, a.streams)
-    model = Model(cfg, w, max_tokens=max_tokens, max_text_len=max(max_tokens, 512), max_texts=1024, device="cuda:0",
+    max_texts = max(1024, max(p.n_texts for p in packs))
+    max_len = max(512, max(int(np.diff(p.offsets).max()) for p in packs))
+    model = Model(cfg, w, max_tokens=max_tokens, max_text_len=max_len, max_texts=max_texts, device="cuda:0",
                   split_k=a.split_k, graph=a.graph)
-    models = [model] + [Model(cfg, None, max_tokens=max_tokens, max_text_len=max(max_tokens, 512), max_texts=1024,
+    models = [model] + [Model(cfg, None, max_tokens=max_tokens, max_text_len=max_len, max_texts=max_texts,
                               device="cuda:0", shared_from=model, split_k=a.split_k, graph=a.graph)
                         for _ in range(S - 1)]
     streams = [torch.cuda.Stream(device=dev) for _ in range(S)]
@@ -234,7 +243,7 @@ def main():
         achieved = flops / (ms_dom / 1e3) / 1e12
         peak = PEAK_TFLOPS[cfg.precision]
         traffic = None
-        if a.workload == "full_bf16_packs2048":
+        if a.workload == "full_bf16_packs2048" and not a.merged:  # the counters' launch shapes
             traffic = traffic_from_profile(
                 os.path.join(ROOT, "transformer_text_embedding_amd", "csrc", "kernels_gemm.hip"),
                 os.path.join(ROOT, "profiles", "traffic_gemm_geglu_full_bf16_packs2048.json"))
@@ -271,11 +280,11 @@ def main():
         "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": round(secs * 1e3 / a.steps, 3), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[cfg.precision], "data": "synthetic",
-        "config": {"workload": a.workload, "packs_per_step": len(packs), "tokens_per_step": tokens_per_step,
+        "config": {"workload": a.workload, "packs_per_step": len(cpu_packs), "tokens_per_step": tokens_per_step,
                    "pack_budget": spec.get("pack_budget"), "layers": cfg.layers, "hidden": cfg.hidden,
                    "heads": cfg.heads, "intermediate": cfg.intermediate, "calls_per_step": len(packs),
                    "streams": S, "hw_queues": int(os.environ.get("GPU_MAX_HW_QUEUES", "4")), "output": a.output,
-                   "split_k": a.split_k, "graph": a.graph,
+                   "split_k": a.split_k, "graph": a.graph, "merged": a.merged,
                    "single_stream_ms_per_step": round(single_ms, 3) if single_ms else None},
         "roofline": roofline,
     }
@@ -283,7 +292,7 @@ def main():
         line["kernels"] = breakdown
     if not a.no_cpu_baseline:
         log("timing the CPU oracle sample")
-        line["cpu_baseline"] = cpu_baseline(a.workload, cfg, w, packs, a.cpu_sample_tokens)
+        line["cpu_baseline"] = cpu_baseline(a.workload, cfg, w, cpu_packs, a.cpu_sample_tokens)
     for m in models:
         m.close()
     print(json.dumps(line), flush=True)
