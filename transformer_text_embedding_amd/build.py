@@ -38,10 +38,14 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build the library)")
 
 
-# Per-source flags.  Attention: matrix-core accumulators in ordinary VGPRs
-# (left to itself the compiler parks the softmax's score and output tiles
-# in AGPRs and moves them back and forth for every VALU touch).
-SOURCE_FLAGS = {"kernels_attn.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+# Per-source flags: matrix-core accumulators in ordinary VGPRs.  Left to
+# itself the compiler parks accumulators in AGPRs whenever a kernel needs
+# more than ~128 registers, and then moves them back and forth for every
+# VALU touch: the attention's softmax, the int8 / 4-bit block-scale FMAs
+# (which became ~50% more VALU instructions).  The bf16 GEMM kernels it
+# leaves byte-identical.
+VGPR_FORM = ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]
+SOURCE_FLAGS = {"kernels_attn.hip": VGPR_FORM, "kernels_gemm.hip": VGPR_FORM}
 
 
 def _compile(src: str) -> str:
