@@ -17,7 +17,10 @@ sample of the same workload on the host's cores.  The roofline comes from a
 second timed pass of the same steps on a single stream with a HIP event pair
 around every launch of the dominant kernel on that stream (with several
 streams, kernels of different packs overlap and per-launch durations would
-include the time they share the chip).
+include the time they share the chip).  An untimed single-stream step with
+event pairs around every launch adds the work rate of each kernel class
+("kernels": TFLOP/s and fraction of peak for the GEMMs and attention, GB/s
+for the row kernels).
 """
 import argparse
 import json
@@ -134,7 +137,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-launch events of the dominant kernel")
-    ap.add_argument("--breakdown", action="store_true", help="add an untimed step timing every kernel class")
+    ap.add_argument("--no-breakdown", dest="breakdown", action="store_false",
+                    help="skip the untimed single-stream step that times every kernel class")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized fp32 buffer 5 times with torch (known bytes, for HBM counter scaling)")
     a = ap.parse_args()
@@ -289,6 +293,9 @@ def main():
         "roofline": roofline,
     }
     if breakdown is not None:
+        # one pack at a time: the residual products' tiles are sized for
+        # packs on concurrent streams, so their lone rate here is low
+        breakdown["measured_in"] = "untimed single-stream step"
         line["kernels"] = breakdown
     if not a.no_cpu_baseline:
         log("timing the CPU oracle sample")
