@@ -13,8 +13,9 @@
  *   - same section, packing paragraph: several texts are processed in one
  *     pass, positions restart in every text and attention never crosses a
  *     text, so a packed call returns the same vectors as one call per text;
- *   - section 精度と量子化: the integer path rounds each activation row to
- *     7 bits with one scale per row and uses the stored weight blocks as is.
+ *   - section 精度と量子化: the integer paths (-q8 and -q4 there) round each
+ *     activation row to 7 bits with one scale per row and use the stored
+ *     weight blocks as they are.
  *
  * Conventions shared by every entry point:
  *   - Every function returns a tte_status.  On failure nothing has been
@@ -159,7 +160,8 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
  * d_out: fp32 [n_texts, H], one unit-norm vector per text (mean over every
  * token of the text, BOS/EOS included, after the final LayerNorm).  Token ids
  * outside [0, vocab) are clamped on the device.  n_texts = 0 with
- * n_tokens = 0 is a no-op. */
+ * n_tokens = 0 is a no-op.  With TTE_FLAG_GRAPH the pass may run as a
+ * replayed graph (see there); the results are the same bits. */
 tte_status tte_embed(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens,
                      const int32_t* h_offsets, int32_t n_texts, float* d_out, void* stream);
 
@@ -190,7 +192,9 @@ tte_status tte_embed_trace(tte_model* m, const int32_t* d_token_ids, int32_t n_t
 tte_status tte_check_pack(const tte_config* cfg, int32_t n_tokens, const int32_t* h_offsets, int32_t n_texts);
 
 /* Free the model (not the borrowed weights or workspace).  Waits for the
- * model's pending offset upload. */
+ * model's pending offset upload; a model with captured graphs
+ * (TTE_FLAG_GRAPH) first synchronises its device, since a replay may still
+ * be running on a caller's stream. */
 tte_status tte_destroy(tte_model* m);
 
 /* Message of the calling thread's last failure ("" if none). */
@@ -222,7 +226,12 @@ typedef enum { TTE_EPI_STORE = 0, TTE_EPI_RESIDUAL = 1, TTE_EPI_GEGLU = 2 } tte_
 /* Y = A * W^T on the matrix cores.  precision selects the operand format:
  * TTE_FP32 (A, W fp32), TTE_BF16 (A, W bf16), TTE_INT8 (A int8 codes with
  * d_a_scale fp32 [M]; W int8 with d_w_scale fp32 [N_w, K/32]; y[m,n] =
- * a_scale[m] * sum_b w_scale[n,b] * (int32 sum over block b)).
+ * a_scale[m] * sum_b w_scale[n,b] * (int32 sum over block b)), TTE_INT4
+ * (A as for TTE_INT8; W packed 4-bit codes, bytes [N_w, K/2], and d_w_scale
+ * pointing to its 16-byte records [N_w, K/128] (see TTE_INT4); y[m,n] =
+ * a_scale[m] * sum_b (es[n,b] * P[m,n,b] - eo[n,b] * S[m,b]) with P the
+ * int32 block product and S the block sum of the activation codes; K a
+ * multiple of 256).
  * epilogue: STORE writes d_c [M, N] (fp32, or bf16 if out_kind is BF16);
  * RESIDUAL adds into fp32 d_c [M, N]; GEGLU takes W with 2N rows and writes
  * d_c[m, n] = GELU(y[m, n]) * y[m, N + n] (erf GELU). */

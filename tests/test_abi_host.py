@@ -47,6 +47,13 @@ def test_split_k_flag_adds_partials_workspace(lib):
     assert b - a == 2 * 2048 * 768 * 4  # two fp32 partial products [max_tokens, H]
 
 
+def test_graph_stats_rejects_null(lib):
+    import ctypes as ct
+    a, b, c = ct.c_int32(0), ct.c_int32(0), ct.c_int64(0)
+    assert lib.tte_graph_stats(None, ct.byref(a), ct.byref(b), ct.byref(c)) == B.TTE_E_INVALID
+    assert B.last_error()
+
+
 def test_graph_flag_accepted_without_extra_workspace(lib):
     """TTE_FLAG_GRAPH keeps its graphs host-side: the workspace is the same."""
     assert B.tte_workspace_size(_cfg(flags=B.TTE_FLAG_GRAPH)) == B.tte_workspace_size(_cfg())
