@@ -267,8 +267,9 @@ tte_status tte_op_attention(tte_model* m, int32_t layer, const void* d_qkv, int3
  * bf16, or int8 codes with d_a_scale fp32 [n_tokens] in TTE_INT8).  Writes
  * d_qk [n_tokens, 3H] with RoPE applied (positions restarting per text,
  * the layer's base) to the Q and K columns 0 .. 2H-1 (columns 2H.. are left
- * untouched), and V transposed into d_vt [H, n_tokens].  fp32 outputs,
- * bf16 in TTE_BF16 (section 何が動くか, encoder and packing paragraphs). */
+ * untouched), and V transposed into d_vt [H, n_tokens] (token order).
+ * fp32 outputs, bf16 in TTE_BF16 (section 何が動くか, encoder and packing
+ * paragraphs). */
 tte_status tte_op_qkv(tte_model* m, int32_t layer, const void* d_a, const float* d_a_scale, int32_t n_tokens,
                       const int32_t* h_offsets, int32_t n_texts, void* d_qk, void* d_vt, void* stream);
 

@@ -20,9 +20,19 @@ struct Seg {
   int start, end;
 };
 
+// Column of token t in a bf16 V^T row: within each aligned group of 32
+// tokens, token 16 h + 4 k + r (h < 2, k < 4, r < 4) sits at 8 k + 4 h + r,
+// so the 8 keys an attention lane multiplies (4 k .. 4 k + 3 and
+// 16 + 4 k .. 16 + 4 k + 3 of a group) are one 16-byte run.  fp32 V^T rows
+// are in token order.
+__host__ __device__ inline int vt_col_bf16(int t) {
+  return (t & ~31) | ((t >> 2) & 3) << 3 | ((t >> 4) & 1) << 2 | (t & 3);
+}
+
 // Extra operands of the QKV projection's epilogue: RoPE of the Q and K
 // columns (positions from the per-token text bounds) and V written
-// transposed, vt[h * 64 + d][t] with row stride vt_stride tokens.
+// transposed, vt[h * 64 + d][col(t)] with row stride vt_stride tokens
+// (col = vt_col_bf16 for bf16, t for fp32).
 struct QkvOut {
   const Seg* seg;
   const float* cos_tab;

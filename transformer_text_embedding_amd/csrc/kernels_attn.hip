@@ -53,7 +53,9 @@ struct AttnCfg {
   static constexpr int LDS = STAGES * TILE;
   static constexpr int ROWS_PER_Q = 1024 / ROWB;      // rows per 1 KB load instruction
   static constexpr int QW = (2 * 64 / ROWS_PER_Q) / 4;  // load instructions per wave per tile
-  static constexpr int ALIGN = 16 / ES;               // key alignment of a V^T row segment
+  // key alignment of a tile's V^T row segment: 16 bytes (fp32), or a whole
+  // 32-token group of the bf16 column order (vt_col_bf16)
+  static constexpr int ALIGN = PREC == P_F32 ? 4 : 32;
 };
 
 template <int PREC, int STAGES, int NQ>
@@ -293,11 +295,9 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
         const uint8_t* vr = Vs + (16 * dt + li) * C::ROWB;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          // keys 32u + 4g .. +3 and 32u + 16 + 4g .. +3 (the key order of pb)
-          const u16x4 lo = *reinterpret_cast<const u16x4*>(vr + (((4 * u + (g >> 1)) ^ (li & 7)) << 4) + ((g & 1) << 3));
-          const u16x4 hi =
-              *reinterpret_cast<const u16x4*>(vr + (((4 * u + 2 + (g >> 1)) ^ (li & 7)) << 4) + ((g & 1) << 3));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, u16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
+          // keys 32u + 4g .. +3 and 32u + 16 + 4g .. +3 (the key order of
+          // pb): columns 32u + 8g .. +7 of the tile in the bf16 V^T order
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(vr + (((4 * u + g) ^ (li & 7)) << 4));
 #pragma unroll
           for (int qt = 0; qt < NQ; ++qt)
             oacc[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pb[qt][u], oacc[qt][dt], 0, 0, 0);
@@ -357,8 +357,9 @@ __global__ __launch_bounds__(256) void k_qkv_prep(const void* __restrict__ in, v
     st(qk_out, a + 32, y * cs + x * sn);
   }
   const size_t v = row + 2 * H + h * 64 + d;
-  st(qo.vt, (size_t)(h * 64 + d) * qo.vt_stride + t, ld(v));
-  st(qo.vt, (size_t)(h * 64 + d + 32) * qo.vt_stride + t, ld(v + 32));
+  const int col = PREC == P_BF16 ? vt_col_bf16(t) : t;
+  st(qo.vt, (size_t)(h * 64 + d) * qo.vt_stride + col, ld(v));
+  st(qo.vt, (size_t)(h * 64 + d + 32) * qo.vt_stride + col, ld(v + 32));
 }
 
 }  // namespace

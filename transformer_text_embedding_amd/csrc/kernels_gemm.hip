@@ -507,7 +507,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
         }
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const size_t at = (size_t)(n_base - 2 * qo.hidden + nt * 16 + li) * qo.vt_stride + mr;
+          // bf16: the 4 tokens (a multiple of 4 apart from the group start)
+          // stay 4 consecutive columns under vt_col_bf16
+          const size_t at = (size_t)(n_base - 2 * qo.hidden + nt * 16 + li) * qo.vt_stride +
+                            (OUT == O_BF16 ? vt_col_bf16(mr) : mr);
           if constexpr (OUT == O_BF16) {
             uint16_t* vp = reinterpret_cast<uint16_t*>(qo.vt) + at;
             if (mr + 3 < M) {

@@ -245,6 +245,15 @@ __global__ void k_seg(const int* __restrict__ off, int n_texts, int T, Seg* __re
   seg[t] = Seg{off[lo], off[lo + 1]};
 }
 
+// bf16 V^T rows from the attention's column order (vt_col_bf16) to token
+// order: out[r][t] = vt[r][col(t)] for r < rows, t < T.
+__global__ void k_vt_tokens(const uint16_t* __restrict__ vt, int stride, uint16_t* __restrict__ out, int T, int rows) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)rows * T) return;
+  const int r = (int)(i / T), t = (int)(i % T);
+  out[i] = vt[(size_t)r * stride + vt_col_bf16(t)];
+}
+
 // The launch sequence of one pass over an uploaded pack.  The output is
 // either the pooled unit vectors (d_out [B, H]) or, with d_tok, the
 // per-token states after the final LayerNorm ([T, H]); d_states receives
@@ -708,11 +717,18 @@ tte_status tte_op_qkv(tte_model* m, int32_t layer, const void* d_a, const float*
   const tte_layer_weights& LW = m->layers[layer];
   const QkvOut qo{m->seg, glob ? m->cosg : m->cosl, glob ? m->sing : m->sinl, m->vt, m->L.vt_stride, H};
   launch_gemm_qkv(P, d_a, d_a_scale, LW.wqkv, LW.wqkv_scale, n_tokens, H, d_qk, P == TTE_BF16 ? O_BF16 : O_F32, qo, s);
-  const size_t es = P == TTE_BF16 ? 2 : 4;
-  st = hip_check(hipMemcpy2DAsync(d_vt, (size_t)n_tokens * es, m->vt, (size_t)m->L.vt_stride * es, (size_t)n_tokens * es,
-                                  (size_t)H, hipMemcpyDeviceToDevice, s),
-                 "hipMemcpy2DAsync(vt)");
-  if (st != TTE_OK) return st;
+  if (P == TTE_BF16) {
+    // back to token order (the workspace copy is in the attention's column
+    // order, vt_col_bf16)
+    const long n = (long)H * n_tokens;
+    k_vt_tokens<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(reinterpret_cast<const uint16_t*>(m->vt), m->L.vt_stride,
+                                                           reinterpret_cast<uint16_t*>(d_vt), n_tokens, H);
+  } else {
+    st = hip_check(hipMemcpy2DAsync(d_vt, (size_t)n_tokens * 4, m->vt, (size_t)m->L.vt_stride * 4,
+                                    (size_t)n_tokens * 4, (size_t)H, hipMemcpyDeviceToDevice, s),
+                   "hipMemcpy2DAsync(vt)");
+    if (st != TTE_OK) return st;
+  }
   return hip_check(hipGetLastError(), "kernel launch");
 }
 
