@@ -541,7 +541,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
   // Other epilogues: the wave's results pass through LDS one 16-row slab at
   // a time (row-major, rows padded by 16 bytes so that the 4 row groups of
   // a write land in different banks) and leave as 16-byte vectors of whole
-  // rows; the residual form reads, adds and writes 16 bytes at a time.
+  // rows; the residual form loads all of its 16-byte chunks of a slab, then
+  // adds and writes them.
   constexpr bool F32_OUT = EPI == E_RESID || EPI == E_PART || OUT == O_F32;
   constexpr int OES = F32_OUT ? 4 : 2;                     // output element bytes
   constexpr int NT_OUT = EPI == E_GEGLU ? WN / 2 : WN;     // 16-column output tiles per wave
@@ -583,6 +584,27 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
     // LDS operations of one wave complete in order: the reads below see the
     // writes above, and the next slab's writes follow these reads
     __builtin_amdgcn_wave_barrier();
+    if constexpr (EPI == E_RESID) {
+      // every load of the slab's rows first, then the stores (the compiler
+      // would otherwise wait for each chunk's load behind the previous store)
+      constexpr int NI = 16 * CPR / 64;
+      static_assert(NI * 64 == 16 * CPR, "whole chunks per lane");
+      f32x4 ov[NI], dv[NI];
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = lane + 64 * i, row = c / CPR, cc = c % CPR, m = m_slab + row;
+        dv[i] = *reinterpret_cast<const f32x4*>(slab + row * RB + cc * 16);
+        ov[i] = m < M ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(C) + (size_t)m * N + n_wave + 4 * cc)
+                      : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int c = lane + 64 * i, row = c / CPR, cc = c % CPR, m = m_slab + row;
+        if (m < M) *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + (size_t)m * N + n_wave + 4 * cc) = ov[i] + dv[i];
+      }
+      __builtin_amdgcn_wave_barrier();
+      continue;
+    }
 #pragma unroll
     for (int c = lane; c < 16 * CPR; c += 64) {
       const int row = c / CPR, cc = c % CPR;
@@ -590,12 +612,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
       if (m >= M) continue;
       const u32x4 d = *reinterpret_cast<const u32x4*>(slab + row * RB + cc * 16);
       const int n = n_wave + cc * (16 / OES);
-      if constexpr (EPI == E_RESID) {
-        f32x4* cp = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + (size_t)m * N + n);
-        f32x4 o = *cp;
-        o += __builtin_bit_cast(f32x4, d);
-        *cp = o;
-      } else if constexpr (EPI == E_PART) {
+      if constexpr (EPI == E_PART) {
         *reinterpret_cast<u32x4*>(reinterpret_cast<float*>(C) + ((size_t)split * M + m) * N + n) = d;
       } else {
         *reinterpret_cast<u32x4*>(reinterpret_cast<uint8_t*>(C) + ((size_t)m * N + n) * OES) = d;
