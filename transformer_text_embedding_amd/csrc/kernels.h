@@ -101,9 +101,10 @@ void launch_qkv_prep(int prec, const void* qkv_in, void* qk_out, const QkvOut& q
 
 // Attention over the packed axis.  qk: [T, 3H] with rotated Q and K in
 // columns 0 .. 2H-1; vt: V transposed [H][vt_stride]; o: [T, H].  fp32 or
-// bf16 operands.
+// bf16 operands.  mean_len: the pack's mean text length (tokens), which
+// picks the query block size.
 void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, void* o, const Seg* seg, int T,
-                      int n_heads, int is_global, int window, hipStream_t s);
+                      int n_heads, int is_global, int window, int mean_len, hipStream_t s);
 
 // Cosine-similarity matrix of unit vectors: sim [n, n] = E E^T, E fp32
 // [n, dim] row-major, dim % 16 == 0.

@@ -14,8 +14,8 @@
 // simply start(q) <= key < end(q); no per-key lookup is needed.
 //
 // How: flash-style streaming over the packed token axis.  A block takes 64
-// consecutive queries (128 on bf16 global layers: 16 or 32 per wave; they
-// may span several texts) and walks 64-key tiles over the union of their
+// consecutive queries (128 on bf16 global layers when the pack's texts
+// average >= 1024 tokens: 16 or 32 per wave; they may span several texts) and walks 64-key tiles over the union of their
 // allowed key ranges only (a local layer needs at most 64 + 2*window keys, a
 // global one the texts of its queries), so fully masked tiles are never
 // loaded; a wave also skips the matrix work of tiles outside its own
@@ -365,7 +365,7 @@ __global__ __launch_bounds__(256) void k_qkv_prep(const void* __restrict__ in, v
 }  // namespace
 
 void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, void* o, const Seg* seg, int T,
-                      int n_heads, int is_global, int window, hipStream_t s) {
+                      int n_heads, int is_global, int window, int mean_len, hipStream_t s) {
   if (T <= 0) return;
   const float scale_log2 = 0.125f * 1.4426950408889634f;
   // a double buffer: deeper rings (3 or 4 stages) measured slower on MI355X
@@ -381,11 +381,13 @@ void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, v
     attr_set = true;
   }
   if (prec == P_BF16) {
-    // global layers: 32 queries per wave (128 per block), each K / V^T
-    // fragment feeding two query tiles (4x4096 texts: 4.22 -> 4.10 ms per
-    // pass); local layers keep 16 (their 128-query blocks span more keys:
-    // 0.58 -> 0.70 ms)
-    if (is_global) {
+    // global layers over long texts: 32 queries per wave (128 per block),
+    // each K / V^T fragment feeding two query tiles (4 texts of 4096: 3.4 ->
+    // 3.0 ms of global attention per pass).  Short texts and local layers
+    // keep 16: a 128-query block spans more texts' keys (packs of texts of
+    // ~190 tokens: 11.5 -> 8.8 ms per 64-pack step with 64-query blocks;
+    // local layers over 4096-token texts: 0.58 -> 0.70 ms with 128).
+    if (is_global && mean_len >= 1024) {
       const dim3 grid((T + 127) / 128, n_heads);
       k_attn<P_BF16, ST, 2><<<grid, 256, AttnCfg<P_BF16, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads,
                                                                         is_global, window, scale_log2);

@@ -306,7 +306,7 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
     {
       ProfScope ps(m, glob ? TTE_K_ATTN_GLOBAL : TTE_K_ATTN_LOCAL, s);
       launch_attention(P == TTE_BF16 ? P_BF16 : P_F32, m->qkv, m->vt, m->L.vt_stride, m->o, m->seg, T, nh, glob,
-                       c.window, s);
+                       c.window, T / B, s);
     }
     const void* o_in = m->o;
     if (integer) {
@@ -694,7 +694,8 @@ tte_status tte_op_attention(tte_model* m, int32_t layer, const void* d_qkv, int3
   const int prec = m->cfg.precision == TTE_BF16 ? P_BF16 : P_F32;
   const QkvOut qo{m->seg, glob ? m->cosg : m->cosl, glob ? m->sing : m->sinl, m->vt, m->L.vt_stride, m->cfg.hidden};
   launch_qkv_prep(prec, d_qkv, m->qkv, qo, n_tokens, s);
-  launch_attention(prec, m->qkv, m->vt, m->L.vt_stride, d_o, m->seg, n_tokens, m->cfg.n_heads, glob, m->cfg.window, s);
+  launch_attention(prec, m->qkv, m->vt, m->L.vt_stride, d_o, m->seg, n_tokens, m->cfg.n_heads, glob, m->cfg.window,
+                   n_tokens / n_texts, s);
   return hip_check(hipGetLastError(), "kernel launch");
 }
 
