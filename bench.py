@@ -21,6 +21,12 @@ include the time they share the chip).  An untimed single-stream step with
 event pairs around every launch adds the work rate of each kernel class
 ("kernels": TFLOP/s and fraction of peak for the GEMMs and attention, GB/s
 for the row kernels).
+
+--row-kernels prints a different line instead: the HBM-bound row kernels
+(LayerNorm fp32 -> bf16 as in front of the bf16 products, and the per-row
+7-bit quantisation of the integer paths) through the C ABI at one pack's
+shape and at a 1 GiB fp32 input, as algorithmic bytes per launch over the
+mean time of back-to-back launches (HIP events on the launching stream).
 """
 import argparse
 import json
@@ -57,6 +63,59 @@ def traffic_from_profile(kernel_source: str, profile: str):
 
 
 HBM_GBS = 8000.0
+
+
+def row_kernels(torch, B, dev, reps=20):
+    """Algorithmic GB/s of LayerNorm (fp32 in, bf16 out, gain read once) and
+    7-bit quantisation (fp32 in, int8 codes and one fp32 scale per row out)
+    at widths of 768, for 1913 rows (a mean pack) and 1 GiB of input."""
+    H = 768
+    s = torch.cuda.current_stream()
+    res = []
+    for rows in (1913, (1 << 30) // (4 * H)):
+        g = torch.Generator(device=dev).manual_seed(7)
+        x = torch.randn(rows, H, device=dev, generator=g)
+        gamma = torch.ones(H, device=dev)
+        out = torch.empty(rows, H, dtype=torch.bfloat16, device=dev)
+        q = torch.empty(rows, H, dtype=torch.int8, device=dev)
+        sc = torch.empty(rows, device=dev)
+        kernels = (
+            ("layernorm fp32 -> bf16", rows * H * (4 + 2) + H * 4,
+             lambda: B.tte_op_layernorm(x.data_ptr(), gamma.data_ptr(), rows, H, 1e-5, B.TTE_OUT_BF16,
+                                        out.data_ptr(), 0, s.cuda_stream)),
+            ("quant7 fp32 -> int8", rows * H * (4 + 1) + rows * 4,
+             lambda: B.tte_op_quant7(x.data_ptr(), rows, H, q.data_ptr(), sc.data_ptr(), s.cuda_stream)),
+        )
+        for name, nbytes, fn in kernels:
+            for _ in range(3):
+                fn()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(s)
+            for _ in range(reps):
+                fn()
+            e1.record(s)
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / reps
+            gbs = nbytes / us / 1e3
+            res.append({"kernel": name, "rows": rows, "width": H, "bytes": nbytes, "us": round(us, 2),
+                        "GB/s": round(gbs, 1), "frac_of_hbm": round(gbs / HBM_GBS, 4)})
+        del x, out, q, sc
+    # the practical ceiling: a plain device copy of 1 GiB (torch), read + write
+    src = torch.ones((1 << 30) // 4, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(s)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(s)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / reps
+    res.append({"kernel": "device copy (torch), reference", "rows": None, "width": None, "bytes": 2 << 30,
+                "us": round(us, 2), "GB/s": round((2 << 30) / us / 1e3, 1),
+                "frac_of_hbm": round((2 << 30) / us / 1e3 / HBM_GBS, 4)})
+    return res
 
 
 def allowed_pairs(lengths, window):
@@ -139,6 +198,8 @@ def main():
                     help="time the steps without the per-launch events of the dominant kernel")
     ap.add_argument("--no-breakdown", dest="breakdown", action="store_false",
                     help="skip the untimed single-stream step that times every kernel class")
+    ap.add_argument("--row-kernels", action="store_true",
+                    help="only measure the row kernels' HBM rate (LayerNorm, 7-bit quantisation) at two shapes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized fp32 buffer 5 times with torch (known bytes, for HBM counter scaling)")
     a = ap.parse_args()
@@ -172,6 +233,13 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_each_way": n * 4, "copies": 5}), flush=True)
+        return
+    if a.row_kernels:
+        res = row_kernels(torch, B, dev)
+        big = [r for r in res if r["kernel"].startswith("layernorm") and r["rows"] > 1913][0]
+        print(json.dumps({"metric": "row kernels: algorithmic HBM GB/s (LayerNorm fp32 -> bf16 at 1 GiB)",
+                          "value": big["GB/s"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
+                          "peak": HBM_GBS, "data": "synthetic", "results": res}), flush=True)
         return
     spec = ti.workload(a.workload)
     cfg = spec["cfg"]
