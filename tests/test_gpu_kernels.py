@@ -430,7 +430,10 @@ def _attn_model(precision, hidden, heads):
     return Model(spec, w, max_tokens=4096, max_text_len=4096, max_texts=64)
 
 
-ATTN_PACKS = [[8, 40, 130], [1, 64, 65, 200, 3, 129], [957], [2048], [5, 3000, 2]]
+# bf16 global layers take 128-query blocks when the texts average >= 1024
+# tokens ([2048], [1100, 1037], [3000, 7]: the last two with ragged tails,
+# and a short text inside the last block), 64-query blocks otherwise
+ATTN_PACKS = [[8, 40, 130], [1, 64, 65, 200, 3, 129], [957], [2048], [5, 3000, 2], [1100, 1037], [3000, 7]]
 
 
 @pytest.mark.parametrize("lengths", ATTN_PACKS)
