@@ -120,10 +120,11 @@ __device__ __forceinline__ int w_row(int r, int nb, int N) {
 // instructions of A/W rows, and for int8 the 16-byte scale vectors of 32 W
 // rows (lanes 0..31 of every wave).
 template <int QW, int PREC, int KT>
-__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* const* src, const int* step,
-                                           const float* s_src, int kt, int wid, int lane, int scale_at) {
+__device__ __forceinline__ void issue_tile(uint8_t* stage, const uint8_t* const* sbase, const uint32_t* soff,
+                                           const int* step, const float* s_src, int kt, int wid, int lane,
+                                           int scale_at) {
 #pragma unroll
-  for (int j = 0; j < QW; ++j) dma16(src[j] + (size_t)kt * step[j], stage + (wid * QW + j) * 1024);
+  for (int j = 0; j < QW; ++j) dma16(sbase[j] + (soff[j] + (uint32_t)(kt * step[j])), stage + (wid * QW + j) * 1024);
   if constexpr (PREC == P_I8 || PREC == P_I4) {
     if (lane < 32) dma16(s_src + kt * 4, stage + scale_at + wid * 512);
   }
@@ -160,7 +161,10 @@ __device__ __forceinline__ long unpack_q4(uint32_t x) {
 }
 
 template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES, int WGM, int WGN, int KT>
-__global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
+// The 128 x 192 bf16 GeGLU tiles (WN = 6) are held to 4 waves per SIMD, 128
+// registers, so that two blocks share a CU (the compiler spills two
+// registers for it); every other shape takes what it needs.
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WN == 6 ? 4 : 1))) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
                                               const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
                                               void* __restrict__ C, int M, int N, int K, int n_blocks,
                                               int m_blocks, int grp, int splits, QkvOut qo) {
@@ -209,25 +213,35 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
   const int lrow = lane / CPRW, slot = lane % CPRW;
   // int4: the W rows are KT/2 bytes (packed codes) and take the 64-byte
   // row plan (16 rows per instruction, 4-chunk swizzle) after the A rows.
-  const uint8_t* src[G::QW];
+  // Each source is a wave-uniform base (the A rows from the block's first
+  // row, or W) plus a 32-bit per-lane byte offset, so the loads take the
+  // scalar-base form and a lane keeps one register per instruction.
+  const uint8_t* sbase[G::QW];
+  uint32_t soff[G::QW];
   int step[G::QW];  // bytes a row advances per K tile
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
+  const uint8_t* a_base = A + (size_t)m0 * row_bytes + (size_t)split * k_part * F::ES;
 #pragma unroll
   for (int j = 0; j < G::QW; ++j) {
-    const int q = wid * G::QW + j;
+    const int q = wid_u * G::QW + j;
     if (G::Q4 && q >= G::QA) {
       const int r = 16 * (q - G::QA) + (lane >> 2);  // W row of the tile
       const int i = lane >> 2;  // r & 15
       const int chunk = (lane & 3) ^ (((i >> 1) ^ (i >> 3)) & 3);
-      src[j] = W + (size_t)w_row<EPI, BN, WGN>(r, nb, N) * (K / 2) + (size_t)split * (k_part / 2) + chunk * 16;
+      sbase[j] = W + (size_t)split * (k_part / 2);
+      soff[j] = (uint32_t)w_row<EPI, BN, WGN>(r, nb, N) * (uint32_t)(K / 2) + chunk * 16;
       step[j] = KT / 2;
       continue;
     }
     const int r = RPI * q + lrow;
     const int chunk = slot ^ (KT == 256 ? (r & 15) : KT == 128 ? (r & 7) : ((((r & 15) >> 1) ^ ((r & 15) >> 3)) & 3));
-    if (r < BM)
-      src[j] = A + (size_t)min(m0 + r, M - 1) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
-    else
-      src[j] = W + (size_t)w_row<EPI, BN, WGN>(r - BM, nb, N) * row_bytes + (size_t)split * k_part * F::ES + chunk * 16;
+    if (RPI * q < BM) {  // the instruction's rows are all A rows or all W rows
+      sbase[j] = a_base;
+      soff[j] = (uint32_t)(min(m0 + r, M - 1) - m0) * (uint32_t)row_bytes + chunk * 16;
+    } else {
+      sbase[j] = W + (size_t)split * k_part * F::ES;
+      soff[j] = (uint32_t)w_row<EPI, BN, WGN>(r - BM, nb, N) * (uint32_t)row_bytes + chunk * 16;
+    }
     step[j] = KT;
   }
   // int8 / int4: lanes 0..31 of wave w load the 16 bytes (int8: 4 block
@@ -258,7 +272,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
     static_assert(KS % 2 == 0, "each tile starts in fragment set 0");
     const int issued0 = min(G::STAGES, nk);
     for (int p = 0; p < issued0; ++p)
-      issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, src, step, s_src, p, wid, lane, G::AREG + G::WREG);
+      issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, sbase, soff, step, s_src, p, wid, lane, G::AREG + G::WREG);
     wait_vm((issued0 - 1) * G::PER_TILE);  // tile 0 has landed (own loads)
     __builtin_amdgcn_s_barrier();          // ... and every wave's
     asm volatile("" ::: "memory");
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
         __builtin_amdgcn_s_barrier();
         asm volatile("" ::: "memory");
         if (kt + G::STAGES < nk)
-          issue_tile<G::QW, PREC, KT>(smem + stg * G::TILE, src, step, s_src, kt + G::STAGES, wid, lane,
+          issue_tile<G::QW, PREC, KT>(smem + stg * G::TILE, sbase, soff, step, s_src, kt + G::STAGES, wid, lane,
                                       G::AREG + G::WREG);
       }
       // k-step 0 of tile kt + 1 is read behind the last k-step's MFMAs of
@@ -315,7 +329,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
 #endif
   {
   for (int p = 0; p < G::STAGES - 1 && p < nk; ++p)
-    issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, src, step, s_src, p, wid, lane, G::AREG + G::WREG);
+    issue_tile<G::QW, PREC, KT>(smem + p * G::TILE, sbase, soff, step, s_src, p, wid, lane, G::AREG + G::WREG);
 
   for (int kt = 0; kt < nk; ++kt) {
     // this wave's loads of tile kt are done once at most `ahead` tiles of
@@ -325,7 +339,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void k_gemm(const uint8_t* __restri
     __builtin_amdgcn_s_barrier();
     // the stage of tile kt - 1 is free: every wave finished reading it
     if (kt + G::STAGES - 1 < nk)
-      issue_tile<G::QW, PREC, KT>(smem + ((kt + G::STAGES - 1) % G::STAGES) * G::TILE, src, step, s_src,
+      issue_tile<G::QW, PREC, KT>(smem + ((kt + G::STAGES - 1) % G::STAGES) * G::TILE, sbase, soff, step, s_src,
                                   kt + G::STAGES - 1, wid, lane, G::AREG + G::WREG);
 
     const uint8_t* stage = smem + (kt % G::STAGES) * G::TILE;
@@ -644,17 +658,17 @@ void go(const void* A, const float* a_scale, const void* W, const float* w_scale
                                                  m_blocks, grp, splits, qo);
 }
 
-template <int PREC, int WM, int ST, int WGM = 2, int WGN = 2, int KT = 128>
+template <int PREC, int WM, int ST, int WGM = 2, int WGN = 2, int KT = 128, int WN = 4>
 void go_prec(int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N, int K,
              void* C, int out_kind, hipStream_t s) {
   if (epi == E_RESID) {
-    go<PREC, E_RESID, O_F32, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
+    go<PREC, E_RESID, O_F32, WM, WN, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
   } else if (epi == E_GEGLU) {
-    if (out_kind == O_BF16) go<PREC, E_GEGLU, O_BF16, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
-    else go<PREC, E_GEGLU, O_F32, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
+    if (out_kind == O_BF16) go<PREC, E_GEGLU, O_BF16, WM, WN, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
+    else go<PREC, E_GEGLU, O_F32, WM, WN, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
   } else {
-    if (out_kind == O_BF16) go<PREC, E_STORE, O_BF16, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
-    else go<PREC, E_STORE, O_F32, WM, 4, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
+    if (out_kind == O_BF16) go<PREC, E_STORE, O_BF16, WM, WN, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
+    else go<PREC, E_STORE, O_F32, WM, WN, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
   }
 }
 
@@ -664,7 +678,9 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
 //    with >= 512 such tiles, and the residual products of >= 8k rows;
 //  * T128W8 / T192W8: 128 x 128 or 192 x 128, 8 waves of 32 x 64 or
 //    48 x 64 (two blocks per CU): every other product (QKV always, GeGLU
-//    below the T256 size, the residual products below 8k rows).  The
+//    below the T256 size, the residual products below 8k rows); GeGLU takes
+//    128 x 192 (32 x 96 waves) instead of 128 x 128 where that fills one
+//    round of 512 blocks.  The
 //    height is the one with the smaller ceil(tiles / 256) * rows, a count
 //    of tile-rows the busiest CU works through (ties to 192: fewer tiles
 //    re-read A less): at 1.9k rows GeGLU runs 803 against 739 TFLOP/s in
@@ -707,7 +723,16 @@ void launch_prec(int epi, const void* A, const float* a_scale, const void* W, co
     case T32: go_prec<PREC, 1, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
     case T64L: go_prec<PREC, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
     case T128W8:
-      if constexpr (PREC == P_BF16) go_prec<PREC, 2, 2, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+      if constexpr (PREC == P_BF16) {
+        // GeGLU: 128 x 192 tiles (8 waves of 32 x 96) where they make one round
+        // of 512 blocks (two per CU) and 192 x 128 tiles would not: at 2048
+        // rows 512 blocks against 528 (or 768 of 128 x 128), 22.7 against
+        // 25.5 us a launch
+        const long t192 = (long)((M + 191) / 192) * (2 * N / 128), tn192 = (long)((M + 127) / 128) * (2 * N / 192);
+        if (epi == E_GEGLU && (2 * N) % 192 == 0 && t192 > 512 && tn192 <= 512)
+          go_prec<PREC, 2, 2, 4, 2, 128, 6>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+        else go_prec<PREC, 2, 2, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+      }
       break;
     case T192W8:
       if constexpr (PREC == P_BF16) go_prec<PREC, 3, 2, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
