@@ -83,8 +83,10 @@ def test_layernorm_to_int8_codes():
 # products of >= 8k rows)
 SHAPES = [(178, 384, 128), (957, 2304, 768), (300, 768, 3072), (130, 512, 256), (1, 128, 128), (4100, 4096, 128),
           (8200, 768, 3072), (1913, 2304, 768)]
+# GeGLU (bf16) at 2001 rows takes the 128 x 192 tiles (512 blocks, where
+# 192 x 128 tiles would make 528), with a ragged last row tile
 GEGLU_SHAPES = [(178, 256, 128), (957, 3072, 768), (65, 64, 256), (2100, 4096, 128), (8192, 3072, 768),
-                (1913, 3072, 768)]
+                (1913, 3072, 768), (2001, 3072, 768)]
 
 
 def _run_gemm(prec, epi, a, a_s, w, w_s, M, N, K, c, out_kind):
