@@ -54,3 +54,14 @@ def test_class_work_gemm_flops_per_token():
     # attention: 9 global layers of 25, 4 * 64 * 12 flops per pair and layer
     g, loc = _brute_pairs([10, 20], 64)
     assert w["attn_global"][0] == g * 3072 * 9 and w["attn_local"][0] == loc * 3072 * 16
+
+
+def test_more_than_one_gpu_is_refused():
+    """bench.py measures one GPU: asked for more it exits with status 2 and a
+    message, before anything touches a device."""
+    import subprocess
+    import sys
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2, (r.returncode, r.stderr)
+    assert "one GPU" in r.stderr and r.stdout == ""
