@@ -290,7 +290,12 @@ typedef enum {
 } tte_kernel_class;
 
 /* Start recording an event pair around every launch whose class bit is set
- * in class_mask, for up to max_launches launches in total. */
+ * in class_mask, for up to max_launches launches in total.  The four
+ * matrix-core product classes record their pair as part of the kernel's
+ * own dispatch (the kernel's execution alone); the other classes record it
+ * as marker packets on the stream around their launches (which adds the
+ * packets' latency).  Calls on a model while recording run eagerly (no
+ * TTE_FLAG_GRAPH replay). */
 tte_status tte_profile_start(tte_model* m, uint32_t class_mask, int32_t max_launches);
 
 /* Wait for the recorded events and return, per class, the summed kernel

@@ -325,3 +325,31 @@ def test_full_size_first_layers_trace(full_models, name, split_k):
         say(f"  {name} state {l}: token cos min {cos.min():.8f} max rel {rel:.2e}")
         gate = {"fp32": 1 - 1e-9, "bf16": 1 - 1e-4, "int8": 1 - 1e-4, "int4": 1 - 1e-4}[cfg.precision]
         assert cos.min() >= gate, (l, cos.min())
+
+
+def test_profile_counts_launches_and_leaves_results_alone():
+    """tte_profile_start / stop around one bf16 pass: one timed launch per
+    layer for each matrix-core class and attention kind, positive times, and
+    the same vectors as the pass without recording."""
+    name = "full_bf16_packs2048"
+    cfg = ti.workload(name)["cfg"]
+    w = ti.cached_storage_weights(cfg)
+    p = ti.make_packs(name)[0]
+    m = Model(cfg, w, max_tokens=2048, max_text_len=2048, max_texts=256)
+    try:
+        ids = dev(p.ids)
+        plain = host(m.embed_pack(ids, p.offsets))
+        B.tte_profile_start(m.handle, (1 << B.TTE_K_COUNT) - 1, 1000)
+        got = host(m.embed_pack(ids, p.offsets))
+        prof = B.tte_profile_stop(m.handle)
+        assert np.array_equal(got, plain)
+        L = cfg.layers
+        n_glob = len([l for l in range(L) if l % cfg.global_every == 0])
+        expect = {"gemm_qkv": L, "gemm_o": L, "gemm_geglu": L, "gemm_o2": L, "attn_global": n_glob,
+                  "attn_local": L - n_glob, "embed": 1, "pool": 1}
+        for k, n in expect.items():
+            ms, launches = prof[k]
+            assert launches == n and ms > 0, (k, ms, launches)
+        say(f"  gemm_geglu {prof['gemm_geglu'][0] * 1e3 / L:.1f} us per launch")
+    finally:
+        m.close()

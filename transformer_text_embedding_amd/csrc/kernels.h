@@ -70,6 +70,16 @@ void launch_ln(const float* x, const float* gamma, int rows, int width, float ep
 // Per-row 7-bit quantisation.
 void launch_quant7(const float* x, int rows, int width, int8_t* q, float* scale, hipStream_t s);
 
+// Timing of the next matrix-core product this thread launches: when set,
+// the product is launched with these events recorded as part of its
+// dispatch (hipExtLaunchKernel) and the slot is cleared, so its measured
+// duration carries no separate marker packets.  Set by the engine's
+// per-launch profiler.
+struct LaunchEvents {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+LaunchEvents& next_gemm_events();
+
 // C = A * W^T with epilogue; see tte_op_gemm.  Requires N % 128 == 0
 // (GEGLU: N % 64 == 0) and K % 128 == 0.
 void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const void* W, const float* w_scale,
