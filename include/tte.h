@@ -290,11 +290,11 @@ typedef enum {
 } tte_kernel_class;
 
 /* Start recording an event pair around every launch whose class bit is set
- * in class_mask, for up to max_launches launches in total.  The four
- * matrix-core product classes record their pair as part of the kernel's
- * own dispatch (the kernel's execution alone); the other classes record it
- * as marker packets on the stream around their launches (which adds the
- * packets' latency).  Calls on a model while recording run eagerly (no
+ * in class_mask, for up to max_launches launches in total.  Every class
+ * but TTE_K_POOL is one kernel per launch and records its pair as part of
+ * that kernel's dispatch (the kernel's execution alone); TTE_K_POOL (two
+ * kernels) records it as marker packets on the stream around them (which
+ * adds the packets' latency).  Calls on a model while recording run eagerly (no
  * TTE_FLAG_GRAPH replay). */
 tte_status tte_profile_start(tte_model* m, uint32_t class_mask, int32_t max_launches);
 

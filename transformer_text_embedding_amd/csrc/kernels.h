@@ -3,6 +3,7 @@
 // pointers non-null, grids in bounds.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -70,15 +71,28 @@ void launch_ln(const float* x, const float* gamma, int rows, int width, float ep
 // Per-row 7-bit quantisation.
 void launch_quant7(const float* x, int rows, int width, int8_t* q, float* scale, hipStream_t s);
 
-// Timing of the next matrix-core product this thread launches: when set,
-// the product is launched with these events recorded as part of its
-// dispatch (hipExtLaunchKernel) and the slot is cleared, so its measured
-// duration carries no separate marker packets.  Set by the engine's
-// per-launch profiler.
+// Timing of the next kernel this thread launches through launch_timed:
+// when set, the kernel is launched with these events recorded as part of
+// its dispatch (hipExtLaunchKernel) and the slot is cleared, so its
+// measured duration is the kernel's alone, with no separate marker
+// packets.  Set by the engine's per-launch profiler.
 struct LaunchEvents {
   hipEvent_t start = nullptr, stop = nullptr;
 };
-LaunchEvents& next_gemm_events();
+LaunchEvents& next_launch_events();
+
+template <typename... KArgs, typename... Args>
+inline void launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32_t shmem, hipStream_t s,
+                         Args... args) {
+  LaunchEvents& ev = next_launch_events();
+  if (ev.start) {
+    const LaunchEvents e = ev;
+    ev = LaunchEvents{};
+    hipExtLaunchKernelGGL(kernel, grid, block, shmem, s, e.start, e.stop, 0u, static_cast<KArgs>(args)...);
+  } else {
+    kernel<<<grid, block, shmem, s>>>(static_cast<KArgs>(args)...);
+  }
+}
 
 // C = A * W^T with epilogue; see tte_op_gemm.  Requires N % 128 == 0
 // (GEGLU: N % 64 == 0) and K % 128 == 0.

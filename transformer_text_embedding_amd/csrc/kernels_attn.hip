@@ -389,16 +389,16 @@ void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, v
     // local layers over 4096-token texts: 0.58 -> 0.70 ms with 128).
     if (is_global && mean_len >= 1024) {
       const dim3 grid((T + 127) / 128, n_heads);
-      k_attn<P_BF16, ST, 2><<<grid, 256, AttnCfg<P_BF16, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads,
+      launch_timed(k_attn<P_BF16, ST, 2>, grid, dim3(256), AttnCfg<P_BF16, ST>::LDS, s, qk, vt, vt_stride, o, seg, T, n_heads,
                                                                         is_global, window, scale_log2);
     } else {
       const dim3 grid((T + 63) / 64, n_heads);
-      k_attn<P_BF16, ST, 1><<<grid, 256, AttnCfg<P_BF16, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads,
+      launch_timed(k_attn<P_BF16, ST, 1>, grid, dim3(256), AttnCfg<P_BF16, ST>::LDS, s, qk, vt, vt_stride, o, seg, T, n_heads,
                                                                         is_global, window, scale_log2);
     }
   } else {
     const dim3 grid((T + 63) / 64, n_heads);
-    k_attn<P_F32, ST, 1><<<grid, 256, AttnCfg<P_F32, ST>::LDS, s>>>(qk, vt, vt_stride, o, seg, T, n_heads, is_global,
+    launch_timed(k_attn<P_F32, ST, 1>, grid, dim3(256), AttnCfg<P_F32, ST>::LDS, s, qk, vt, vt_stride, o, seg, T, n_heads, is_global,
                                                                   window, scale_log2);
   }
 }

@@ -47,8 +47,6 @@
 // columns are up-projection rows n (the GELU half) and the second half rows
 // I + n (the gate half): the two halves of one output land in the same lane
 // and combine in registers, and the [M, 2I] intermediate is never stored.
-#include <hip/hip_ext.h>
-
 #include <algorithm>
 #include <cmath>
 
@@ -655,19 +653,9 @@ void go(const void* A, const float* a_scale, const void* W, const float* w_scale
   // grp = sqrt(per BM / BN)
   const double per = (double)n_blocks * m_blocks / 8.0;
   const int grp = std::max(1, std::min(n_blocks, (int)std::lround(std::sqrt(per * G::BM / G::BN))));
-  const dim3 grid(n_blocks * m_blocks * splits), block(G::THREADS);
-  const uint8_t* a8 = reinterpret_cast<const uint8_t*>(A);
-  const uint8_t* w8 = reinterpret_cast<const uint8_t*>(W);
-  LaunchEvents& ev = next_gemm_events();
-  if (ev.start) {
-    const LaunchEvents e = ev;
-    ev = LaunchEvents{};
-    hipExtLaunchKernelGGL((k_gemm<PREC, EPI, OUT, WM, WN, STAGES, WGM, WGN, KT>), grid, block, G::LDS, s, e.start,
-                          e.stop, 0u, a8, a_scale, w8, w_scale, C, M, N, K, n_blocks, m_blocks, grp, splits, qo);
-  } else {
-    k_gemm<PREC, EPI, OUT, WM, WN, STAGES, WGM, WGN, KT><<<grid, block, G::LDS, s>>>(
-        a8, a_scale, w8, w_scale, C, M, N, K, n_blocks, m_blocks, grp, splits, qo);
-  }
+  launch_timed(k_gemm<PREC, EPI, OUT, WM, WN, STAGES, WGM, WGN, KT>, dim3(n_blocks * m_blocks * splits),
+               dim3(G::THREADS), G::LDS, s, reinterpret_cast<const uint8_t*>(A), a_scale,
+               reinterpret_cast<const uint8_t*>(W), w_scale, C, M, N, K, n_blocks, m_blocks, grp, splits, qo);
 }
 
 template <int PREC, int WM, int ST, int WGM = 2, int WGN = 2, int KT = 128, int WN = 4>
@@ -772,10 +760,6 @@ void launch_qkv_prec(const void* A, const float* a_scale, const void* W, const f
 
 }  // namespace
 
-LaunchEvents& next_gemm_events() {
-  thread_local LaunchEvents e;
-  return e;
-}
 
 void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
                  int N, int K, void* C, int out_kind, hipStream_t s) {

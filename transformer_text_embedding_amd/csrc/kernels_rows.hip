@@ -348,13 +348,13 @@ void launch_embed_ln(int prec, const int32_t* ids, const PackIO* io, int T, cons
   const dim3 grid((T + 3) / 4), block(256);
 #define L_EMB(E)                                                                                                    \
   if (prec == P_F32)                                                                                                \
-    k_embed_ln<E, P_F32><<<grid, block, 0, s>>>(ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, \
+    launch_timed(k_embed_ln<E, P_F32>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, \
                                                  x, seg);                                                           \
   else if (prec == P_BF16)                                                                                          \
-    k_embed_ln<E, P_BF16><<<grid, block, 0, s>>>(ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, \
+    launch_timed(k_embed_ln<E, P_BF16>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, \
                                                   x, seg);                                                          \
   else                                                                                                              \
-    k_embed_ln<E, P_I8><<<grid, block, 0, s>>>(ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x, \
+    launch_timed(k_embed_ln<E, P_I8>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x, \
                                                 seg);
   TTE_EPL_DISPATCH(H, L_EMB)
 #undef L_EMB
@@ -366,13 +366,13 @@ void launch_ln(const float* x, const float* gamma, int rows, int width, float ep
   const dim3 grid((rows + 3) / 4), block(256);
 #define L_LN(E)                                                                                        \
   if (gamma) {                                                                                         \
-    if (out_kind == O_F32) k_ln<E, O_F32, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io);   \
-    else if (out_kind == O_BF16) k_ln<E, O_BF16, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io); \
-    else k_ln<E, O_I8, true><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io);              \
+    if (out_kind == O_F32) launch_timed(k_ln<E, O_F32, true>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);   \
+    else if (out_kind == O_BF16) launch_timed(k_ln<E, O_BF16, true>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io); \
+    else launch_timed(k_ln<E, O_I8, true>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);              \
   } else {                                                                                             \
-    if (out_kind == O_F32) k_ln<E, O_F32, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io);  \
-    else if (out_kind == O_BF16) k_ln<E, O_BF16, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io); \
-    else k_ln<E, O_I8, false><<<grid, block, 0, s>>>(x, gamma, rows, eps, out, out_scale, io);             \
+    if (out_kind == O_F32) launch_timed(k_ln<E, O_F32, false>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);  \
+    else if (out_kind == O_BF16) launch_timed(k_ln<E, O_BF16, false>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io); \
+    else launch_timed(k_ln<E, O_I8, false>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);             \
   }
   TTE_EPL_DISPATCH(width, L_LN)
 #undef L_LN
@@ -388,21 +388,21 @@ void launch_resid_ln(float* x, const float* partials, int splits, const float* g
   const dim3 grid((rows + 3) / 4), block(256);
 #define L_RLN(E)                                                                                                      \
   if (out_kind < 0) {                                                                                                 \
-    k_resid_ln<E, O_F32, false, false><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);  \
+    launch_timed(k_resid_ln<E, O_F32, false, false>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);  \
   } else if (gamma) {                                                                                                 \
     if (out_kind == O_F32)                                                                                            \
-      k_resid_ln<E, O_F32, true, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);  \
+      launch_timed(k_resid_ln<E, O_F32, true, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);  \
     else if (out_kind == O_BF16)                                                                                      \
-      k_resid_ln<E, O_BF16, true, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale); \
+      launch_timed(k_resid_ln<E, O_BF16, true, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale); \
     else                                                                                                              \
-      k_resid_ln<E, O_I8, true, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);   \
+      launch_timed(k_resid_ln<E, O_I8, true, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);   \
   } else {                                                                                                            \
     if (out_kind == O_F32)                                                                                            \
-      k_resid_ln<E, O_F32, false, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale); \
+      launch_timed(k_resid_ln<E, O_F32, false, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale); \
     else if (out_kind == O_BF16)                                                                                      \
-      k_resid_ln<E, O_BF16, false, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);\
+      launch_timed(k_resid_ln<E, O_BF16, false, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);\
     else                                                                                                              \
-      k_resid_ln<E, O_I8, false, true><<<grid, block, 0, s>>>(x, partials, splits, gamma, rows, eps, out, out_scale);  \
+      launch_timed(k_resid_ln<E, O_I8, false, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);  \
   }
   TTE_EPL_DISPATCH(width, L_RLN)
 #undef L_RLN
@@ -416,6 +416,11 @@ void launch_pool(const float* x, const float* gamma, float eps, int H, const int
   k_pool_finish<E * 64><<<n_texts, 256, 0, s>>>(partial, d_off, d_unit, out, io);
   TTE_EPL_DISPATCH(H, L_POOL)
 #undef L_POOL
+}
+
+LaunchEvents& next_launch_events() {
+  thread_local LaunchEvents e;
+  return e;
 }
 
 }  // namespace tte

@@ -173,16 +173,16 @@ struct tte_model {
 
 namespace {
 
-// An event pair around the launches of one kernel class.  The matrix-core
-// products take their pair as part of their own dispatch (next_gemm_events),
-// so their durations are the kernels' alone; other classes record the pair
-// as marker packets on the stream around their launches.
+// An event pair around the launch of one kernel class.  A class that is one
+// kernel takes its pair as part of that kernel's dispatch
+// (next_launch_events), so its duration is the kernel's alone; pooling (two
+// kernels) records the pair as marker packets on the stream around them.
 struct ProfScope {
   tte_model* m;
   hipStream_t s;
   int idx;
-  bool gemm;
-  ProfScope(tte_model* m_, int cls, hipStream_t s_) : m(m_), s(s_), idx(-1), gemm(false) {
+  bool in_dispatch;
+  ProfScope(tte_model* m_, int cls, hipStream_t s_) : m(m_), s(s_), idx(-1), in_dispatch(false) {
     if (!m->prof_on || !(m->prof_mask & (1u << cls))) return;
     if (2 * (m->ev_used + 1) > (int)m->ev.size()) {
       m->ev_overflow = true;
@@ -190,18 +190,18 @@ struct ProfScope {
     }
     idx = m->ev_used++;
     m->ev_cls[idx] = cls;
-    gemm = cls == TTE_K_GEMM_QKV || cls == TTE_K_GEMM_O || cls == TTE_K_GEMM_GEGLU || cls == TTE_K_GEMM_O2;
-    if (gemm) next_gemm_events() = LaunchEvents{m->ev[2 * idx], m->ev[2 * idx + 1]};
+    in_dispatch = cls != TTE_K_POOL;
+    if (in_dispatch) next_launch_events() = LaunchEvents{m->ev[2 * idx], m->ev[2 * idx + 1]};
     else (void)hipEventRecord(m->ev[2 * idx], s);
   }
   ~ProfScope() {
     if (idx < 0) return;
-    if (!gemm) {
+    if (!in_dispatch) {
       (void)hipEventRecord(m->ev[2 * idx + 1], s);
       return;
     }
-    LaunchEvents& e = next_gemm_events();
-    if (e.start) {  // no product was launched (an empty pack): an empty pair
+    LaunchEvents& e = next_launch_events();
+    if (e.start) {  // nothing was launched (an empty pack): an empty pair
       (void)hipEventRecord(e.start, s);
       (void)hipEventRecord(e.stop, s);
       e = LaunchEvents{};
