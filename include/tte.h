@@ -77,8 +77,10 @@ typedef enum {
    * and extra HBM traffic, which lowers throughput when several calls
    * already share the GPU on concurrent streams, so it is off by default. */
   TTE_FLAG_SPLIT_K = 1,
-  /* HIP-graph replay of the pass (the page's section on batching keeps a
-   * pool of graphs keyed by batch size; here the key is the pack's shape).
+  /* HIP-graph replay of the pass.  Prior art: the xujun.org note on 58.com's
+   * multimodal (VLM) inference optimisation, section 4.3 (CUDA graphs for
+   * the ViT module), records the launch sequence once and keeps a pool of
+   * graphs keyed by batch size; here the key is the pack's shape.
    * tte_embed and tte_embed_tokens record, per model, the shapes
    * (n_tokens, n_texts, pool units = sum over texts of ceil(len / 32),
    * output kind) they are called with; at a shape's second call on a
@@ -139,7 +141,12 @@ typedef struct tte_model tte_model;
 
 /* Bytes of device workspace a model of this config needs (activations,
  * per-token text bounds, RoPE tables, pooling partials).  *bytes is set on
- * success. */
+ * success; nothing else happens (no GPU is needed).
+ * Passage: tensai "テキスト埋め込み", section 精度と量子化, speed table and
+ * the sentence after it: loading the model is the slow, one-time step and
+ * memory is sized then; embedding reuses it.  Errors: TTE_E_INVALID for a
+ * config the library cannot run (the message names the field) or a NULL
+ * bytes. */
 tte_status tte_workspace_size(const tte_config* cfg, size_t* bytes);
 
 /* Create a model over BORROWED device weights and a BORROWED device
@@ -147,11 +154,22 @@ tte_status tte_workspace_size(const tte_config* cfg, size_t* bytes);
  * must outlive the model.  Writes the RoPE tables into the workspace
  * (synchronously) and allocates a small pinned host staging area.  Several
  * models may share one set of weights; use one model per concurrent stream.
- * Returns TTE_E_DEVICE when no GPU is present. */
+ * Passage: tensai "テキスト埋め込み", section 何が動くか, encoder
+ * paragraph (the layers and the global / local schedule this config
+ * describes) and section サーバー (requests are stateless and may run
+ * concurrently: one model per stream over shared weights).  Errors:
+ * TTE_E_INVALID for a bad config, a NULL required weight or a misaligned
+ * workspace; TTE_E_NOMEM if the workspace is too small or host memory runs
+ * out; TTE_E_DEVICE when no GPU is present.  *out is NULL on failure. */
 tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_workspace,
                       size_t workspace_bytes, tte_model** out);
 
-/* Embed one pack.  d_token_ids: int32 [n_tokens] on the device, the texts
+/* Embed one pack.  Passage: tensai "テキスト埋め込み", section サーバー
+ * (token ids in, one float32 vector per input text out, <s> and </s>
+ * counted as tokens) and section 何が動くか, pooling paragraph (mean over
+ * the text, unit length) and packing paragraph (texts packed into one pass
+ * give the same vectors as one text at a time).
+ * d_token_ids: int32 [n_tokens] on the device, the texts
  * concatenated.  h_offsets: host int32 [n_texts + 1], offsets[0] = 0,
  * strictly increasing (no empty text), offsets[n_texts] = n_tokens, every
  * text at most max_text_len tokens, n_tokens <= max_tokens, n_texts <=
@@ -193,8 +211,10 @@ tte_status tte_check_pack(const tte_config* cfg, int32_t n_tokens, const int32_t
 
 /* Free the model (not the borrowed weights or workspace).  Waits for the
  * model's pending offset upload; a model with captured graphs
- * (TTE_FLAG_GRAPH) first synchronises its device, since a replay may still
- * be running on a caller's stream. */
+ * (TTE_FLAG_GRAPH) first waits for each graph's last replay, since it may
+ * still be running on a caller's stream.  Passage: the counterpart of
+ * tte_create (section 精度と量子化 of the tensai page: the model is loaded
+ * once and then serves many requests).  Errors: TTE_E_INVALID for NULL. */
 tte_status tte_destroy(tte_model* m);
 
 /* Message of the calling thread's last failure ("" if none). */

@@ -118,6 +118,31 @@ def test_op_gemm_shape_checks_need_no_gpu(lib):
     assert st == B.TTE_E_INVALID
 
 
+@pytest.mark.parametrize("prec,epi,N,K,ok", [
+    # the kernels address W rows with 32-bit byte offsets: W must stay below 4 GiB
+    (B.TTE_FP32, B.TTE_EPI_STORE, 32768, 32768, False),     # 2^32 bytes
+    (B.TTE_FP32, B.TTE_EPI_STORE, 32768 - 128, 32768, True),
+    (B.TTE_BF16, B.TTE_EPI_STORE, 65536, 32768, False),     # 2^32 bytes
+    (B.TTE_BF16, B.TTE_EPI_STORE, 65536 - 128, 32768, True),
+    (B.TTE_BF16, B.TTE_EPI_GEGLU, 32768, 32768, False),     # 2N rows: 2^32 bytes
+    (B.TTE_BF16, B.TTE_EPI_GEGLU, 32768 - 64, 32768, True),
+    (B.TTE_INT8, B.TTE_EPI_STORE, 1 << 20, 4096, False),    # 2^32 bytes
+    (B.TTE_INT4, B.TTE_EPI_STORE, 1 << 20, 8192, False),    # 4-bit codes: K/2 bytes a row, 2^32
+    (B.TTE_INT4, B.TTE_EPI_STORE, 1 << 20, 4096, True),
+])
+def test_op_gemm_refuses_weights_beyond_32bit_offsets(lib, prec, epi, N, K, ok):
+    """Refused before anything is launched: fake non-null pointers are never
+    dereferenced on either path here (the accepted shapes stop at M = 0)."""
+    fake = ctypes.c_void_p(256)
+    st = lib.tte_op_gemm(prec, epi, fake, fake, fake, fake, 0 if ok else 16, N, K, fake, 0, None)
+    assert st == (B.TTE_OK if ok else B.TTE_E_UNSUPPORTED), (st, B.last_error())
+    if not ok:
+        assert "32-bit" in B.last_error()
+    if epi == B.TTE_EPI_STORE and not ok:
+        st = lib.tte_op_gemm_splitk(prec, fake, fake, fake, fake, 16, N, K, 1, fake, None)
+        assert st == B.TTE_E_UNSUPPORTED and "32-bit" in B.last_error()
+
+
 @pytest.mark.skipif(gpu_available(), reason="checks the no-device path")
 def test_create_without_device_reports_device_error(lib):
     cfg = _cfg()

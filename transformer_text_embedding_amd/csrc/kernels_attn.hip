@@ -34,6 +34,8 @@
 // with P rounded to bf16, its per-query sum taken on the matrix cores too
 // (against an all-ones block, so numerator and denominator use the same
 // rounded P), and all statistics in fp32.
+#include <mutex>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -370,16 +372,17 @@ void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, v
   const float scale_log2 = 0.125f * 1.4426950408889634f;
   // a double buffer: deeper rings (3 or 4 stages) measured slower on MI355X
   constexpr int ST = 2;
-  static bool attr_set = false;  // dynamic LDS above 64 KB must be allowed once
-  if (!attr_set) {
+  // dynamic LDS above 64 KB must be allowed once (call_once: several host
+  // threads may launch at the same time)
+  static std::once_flag attr_once;
+  std::call_once(attr_once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_BF16, ST, 1>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, AttnCfg<P_BF16, ST>::LDS);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_BF16, ST, 2>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, AttnCfg<P_BF16, ST>::LDS);
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn<P_F32, ST, 1>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, AttnCfg<P_F32, ST>::LDS);
-    attr_set = true;
-  }
+  });
   if (prec == P_BF16) {
     // global layers over long texts: 32 queries per wave (128 per block),
     // each K / V^T fragment feeding two query tiles (4 texts of 4096: 3.4 ->

@@ -49,6 +49,7 @@
 // and combine in registers, and the [M, 2I] intermediate is never stored.
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "common.h"
 #include "kernels.h"
@@ -640,12 +641,12 @@ template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES = 4, int WGM = 
 void go(const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N, int K, void* C,
         hipStream_t s, const QkvOut& qo = QkvOut{}, int splits = 1) {
   using G = Cfg<WM, WN, PREC, STAGES, WGM, WGN, KT>;
-  static bool attr_set = false;  // once per instantiation
-  if (!attr_set) {
+  // once per instantiation, safe when several host threads launch at once
+  static std::once_flag attr_once;
+  std::call_once(attr_once, [] {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&k_gemm<PREC, EPI, OUT, WM, WN, STAGES, WGM, WGN, KT>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, G::LDS);
-    attr_set = true;
-  }
+  });
   const int n_blocks = EPI == E_GEGLU ? N / (G::BN / 2) : N / G::BN;
   const int m_blocks = (M + G::BM - 1) / G::BM;
   // group width: an XCD's run of per = tiles/8 tiles reads about

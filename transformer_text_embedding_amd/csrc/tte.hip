@@ -103,6 +103,15 @@ bool check_config(const tte_config* c, std::string* why) {
   return true;
 }
 
+// The GEMM kernels address a W row as a 32-bit byte offset from W's base
+// (row * row bytes + the K tile's offset): every byte of W must lie below
+// 2^32.  n_w = rows of W (2N for the GeGLU product).
+bool weight_offsets_fit(int precision, int64_t n_w, int64_t K) {
+  const int64_t bytes_per_k = precision == TTE_FP32 ? 4 : precision == TTE_BF16 ? 2 : 1;
+  const int64_t row = precision == TTE_INT4 ? K / 2 : K * bytes_per_k;
+  return n_w * row <= (int64_t)UINT32_MAX;
+}
+
 tte_status check_pack(const tte_config& c, int32_t n_tokens, const int32_t* h_off, int32_t n_texts) {
   if (n_texts < 0 || n_tokens < 0) return fail(TTE_E_INVALID, "n_texts and n_tokens must be >= 0");
   if (n_texts == 0) {
@@ -163,6 +172,7 @@ struct tte_model {
   struct GraphEntry {
     int kind, T, B, units;
     hipGraphExec_t exec;  // null until the shape's second call
+    hipEvent_t done;      // recorded after each replay: the last one has ended once it completes
     bool failed;          // capture did not succeed: run eagerly
     uint64_t used;
   };
@@ -377,8 +387,27 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
 
 constexpr size_t MAX_GRAPHS = 64;
 
+// Releases a captured graph once its last replay has ended: waits on the
+// event recorded behind that replay on its stream (no other stream is
+// waited for).  The graph is released even if the wait reports an error.
+tte_status release_graph(tte_model::GraphEntry& g) {
+  tte_status st = TTE_OK;
+  if (g.done) {
+    st = hip_check(hipEventSynchronize(g.done), "hipEventSynchronize(graph replay)");
+    (void)hipEventDestroy(g.done);
+    g.done = nullptr;
+  }
+  if (g.exec) {
+    const tte_status d = hip_check(hipGraphExecDestroy(g.exec), "hipGraphExecDestroy");
+    if (st == TTE_OK) st = d;
+    g.exec = nullptr;
+  }
+  return st;
+}
+
 // TTE_FLAG_GRAPH: the entry of a pack shape (inserted at its first call,
-// the least recently used one dropped beyond MAX_GRAPHS).
+// the least recently used one dropped beyond MAX_GRAPHS).  Returns null if
+// dropping the old entry failed (the error is in tte_last_error).
 tte_model::GraphEntry* graph_entry(tte_model* m, int kind, int T, int B, int units, bool* fresh) {
   *fresh = false;
   for (auto& g : m->graphs)
@@ -387,14 +416,12 @@ tte_model::GraphEntry* graph_entry(tte_model* m, int kind, int T, int B, int uni
     size_t lru = 0;
     for (size_t i = 1; i < m->graphs.size(); ++i)
       if (m->graphs[i].used < m->graphs[lru].used) lru = i;
-    if (m->graphs[lru].exec) {
-      // an earlier replay of it may still run on some stream
-      (void)hipDeviceSynchronize();
-      (void)hipGraphExecDestroy(m->graphs[lru].exec);
-    }
+    // an earlier replay of it may still run on the stream it was launched on
+    const tte_status st = release_graph(m->graphs[lru]);
     m->graphs.erase(m->graphs.begin() + lru);
+    if (st != TTE_OK) return nullptr;
   }
-  m->graphs.push_back(tte_model::GraphEntry{kind, T, B, units, nullptr, false, ++m->graph_clock});
+  m->graphs.push_back(tte_model::GraphEntry{kind, T, B, units, nullptr, nullptr, false, ++m->graph_clock});
   *fresh = true;
   return &m->graphs.back();
 }
@@ -429,6 +456,7 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
   if (graph) {
     bool fresh = false;
     tte_model::GraphEntry* e = graph_entry(m, d_tok ? 1 : 0, T, B, n_units, &fresh);
+    if (!e) return TTE_E_DEVICE;
     e->used = ++m->graph_clock;
     if (!fresh && !e->exec && !e->failed) {
       // second call of this shape: record the sequence (nothing runs while
@@ -440,16 +468,21 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
         err = hipStreamEndCapture(s, &g);
         if (err == hipSuccess) err = hipGraphInstantiate(&e->exec, g, nullptr, nullptr, 0);
         if (g) (void)hipGraphDestroy(g);
+        if (err == hipSuccess) err = hipEventCreateWithFlags(&e->done, hipEventDisableTiming);
       }
       (void)hipGetLastError();
       if (err != hipSuccess) {
+        if (e->exec) (void)hipGraphExecDestroy(e->exec);
         e->exec = nullptr;
+        e->done = nullptr;
         e->failed = true;  // this shape runs eagerly from now on
       }
     }
     if (e->exec) {
       ++m->graph_replays;
-      return hip_check(hipGraphLaunch(e->exec, s), "hipGraphLaunch");
+      st = hip_check(hipGraphLaunch(e->exec, s), "hipGraphLaunch");
+      if (st != TTE_OK) return st;
+      return hip_check(hipEventRecord(e->done, s), "hipEventRecord(graph replay)");
     }
   }
   enqueue_pass(m, d_ids, io, T, B, n_units, d_out, d_states, n_run, d_tok, s);
@@ -603,17 +636,16 @@ tte_status tte_destroy(tte_model* m) {
   }
   (void)hipHostFree(m->h_stage);
   for (hipEvent_t e : m->ev) (void)hipEventDestroy(e);
-  bool any_graph = false;
-  for (auto& g : m->graphs) any_graph |= g.exec != nullptr;
-  if (any_graph) {
-    // replays may still be running on the caller's streams
-    (void)hipSetDevice(m->device);
-    (void)hipDeviceSynchronize();
-    for (auto& g : m->graphs)
-      if (g.exec) (void)hipGraphExecDestroy(g.exec);
+  // replays may still be running on the caller's streams: each graph waits
+  // for its own last replay
+  tte_status st = TTE_OK;
+  if (!m->graphs.empty()) (void)hipSetDevice(m->device);
+  for (auto& g : m->graphs) {
+    const tte_status r = release_graph(g);
+    if (st == TTE_OK) st = r;
   }
   delete m;
-  return TTE_OK;
+  return st;
 }
 
 tte_status tte_op_layernorm(const float* d_x, const float* d_gamma, int32_t rows, int32_t width, float eps,
@@ -650,6 +682,8 @@ tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, con
     return fail(TTE_E_UNSUPPORTED, "N must be a multiple of 128 (64 for GEGLU)");
   if (out_kind != TTE_OUT_F32 && out_kind != TTE_OUT_BF16) return fail(TTE_E_INVALID, "out_kind must be F32 or BF16");
   if (epilogue == TTE_EPI_RESIDUAL && out_kind != TTE_OUT_F32) return fail(TTE_E_INVALID, "RESIDUAL needs fp32 C");
+  if (!weight_offsets_fit(precision, epilogue == TTE_EPI_GEGLU ? 2 * (int64_t)N : N, K))
+    return fail(TTE_E_UNSUPPORTED, "W is 4 GiB or larger (the kernels address its rows with 32-bit byte offsets)");
   if (M == 0) return TTE_OK;
   if (!d_a || !d_w || !d_c) return fail(TTE_E_INVALID, "NULL buffer");
   if (precision >= TTE_INT8 && (!d_a_scale || !d_w_scale)) return fail(TTE_E_INVALID, "int8 / int4 need both scales");
@@ -669,6 +703,8 @@ tte_status tte_op_gemm_splitk(int32_t precision, const void* d_a, const float* d
   if (N % 128 != 0 || K % splits != 0 || ((K / splits) * es) % 128 != 0)
     return fail(TTE_E_UNSUPPORTED, "N must be a multiple of 128 and each K part a multiple of 128 bytes");
   if (precision == TTE_INT4 && K % 256 != 0) return fail(TTE_E_UNSUPPORTED, "TTE_INT4 needs K a multiple of 256");
+  if (!weight_offsets_fit(precision, N, K))
+    return fail(TTE_E_UNSUPPORTED, "W is 4 GiB or larger (the kernels address its rows with 32-bit byte offsets)");
   if (M == 0) return TTE_OK;
   if (!d_a || !d_w || !d_partials || (precision >= TTE_INT8 && (!d_a_scale || !d_w_scale)))
     return fail(TTE_E_INVALID, "NULL buffer");
