@@ -13,6 +13,7 @@ from .encoder import (  # noqa: F401
     encode,
     encode_layers,
     encode_tokens,
+    encoder_layer,
     gelu,
     geglu,
     layer_norm,

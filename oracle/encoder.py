@@ -317,10 +317,31 @@ def _project(x: np.ndarray, layer: dict, name: str, precision: str) -> np.ndarra
 # the whole pass
 # --------------------------------------------------------------------------
 
+def encoder_layer(cfg: dict, w: dict, l: int, x: np.ndarray, offsets) -> np.ndarray:
+    """Layer l applied to the residual stream x [T, H] of a pack (section
+    何が動くか, encoder paragraph): pre-norm attention (no norm on layer 0;
+    global with RoPE base 160000 when l is a multiple of global_every, else
+    the +-window local form with base 10000), its output projection added
+    to x; then pre-norm GeGLU feed-forward added to x."""
+    H, nh, d = cfg["hidden"], cfg["heads"], cfg["head_dim"]
+    prec = cfg["precision"]
+    off = np.asarray(offsets, dtype=np.int64)
+    x = np.asarray(x, dtype=np.float64)
+    layer = w["layers"][l]
+    is_global = (l % cfg["global_every"]) == 0
+    base = cfg["rope_base_global"] if is_global else cfg["rope_base_local"]
+    a = x if l == 0 else layer_norm(x, layer["attn_norm"], cfg["ln_eps"])
+    qkv = _project(a, layer, "wqkv", prec)
+    o = attention(qkv, off, nh, d, is_global, cfg["window"], base)
+    x = x + _project(o, layer, "wo", prec)
+    m = layer_norm(x, layer["mlp_norm"], cfg["ln_eps"])
+    y = geglu(_project(m, layer, "wi", prec))
+    return x + _project(y, layer, "wo2", prec)
+
+
 def encode_layers(cfg: dict, w: dict, ids, offsets, n_layers: Optional[int] = None) -> List[np.ndarray]:
     """Hidden states of the residual stream: after the embedding LayerNorm and
     after each layer (fp64 [T, H] each).  n_layers limits the depth."""
-    H, nh, d = cfg["hidden"], cfg["heads"], cfg["head_dim"]
     prec = cfg["precision"]
     ids = np.asarray(ids, dtype=np.int64)
     off = validate_offsets(offsets, len(ids))
@@ -331,16 +352,7 @@ def encode_layers(cfg: dict, w: dict, ids, offsets, n_layers: Optional[int] = No
     states = [x]
     L = cfg["layers"] if n_layers is None else n_layers
     for l in range(L):
-        layer = w["layers"][l]
-        is_global = (l % cfg["global_every"]) == 0
-        base = cfg["rope_base_global"] if is_global else cfg["rope_base_local"]
-        a = x if l == 0 else layer_norm(x, layer["attn_norm"], cfg["ln_eps"])
-        qkv = _project(a, layer, "wqkv", prec)
-        o = attention(qkv, off, nh, d, is_global, cfg["window"], base)
-        x = x + _project(o, layer, "wo", prec)
-        m = layer_norm(x, layer["mlp_norm"], cfg["ln_eps"])
-        y = geglu(_project(m, layer, "wi", prec))
-        x = x + _project(y, layer, "wo2", prec)
+        x = encoder_layer(cfg, w, l, x, off)
         states.append(x)
     return states
 
