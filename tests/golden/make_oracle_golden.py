@@ -1,6 +1,6 @@
 """Write the oracle's expected embeddings for the full-size workloads.
 
-Usage: python tests/golden/make_oracle_golden.py [workload ...]
+Usage: python tests/golden/make_oracle_golden.py [workload ... | spread]
 
 Calls only the CPU oracle (oracle/) on the seeded inputs of tte_inputs, and
 stores the fp64 unit vectors with fingerprints of the inputs they came from
@@ -27,7 +27,7 @@ import tte_inputs as ti  # noqa: E402
 SELECTION = {
     "full_fp32_957": [(0, None)],
     "full_bf16_packs2048": [(0, None), (1, None)],
-    "full_bf16_4x4096": [(0, [0])],
+    "full_bf16_4x4096": [(0, [0, 1, 2, 3])],
     "full_int8_packs2048": [(0, None), (1, None)],
     "full_int4_packs2048": [(0, None)],
 }
@@ -59,7 +59,37 @@ def expected(name, pack_index, texts):
     return emb, fingerprint(cfg, w, pack, texts)
 
 
+# integer workloads -> pack whose fp32-rounding spread is stored: how far the
+# oracle's own pass moves when every intermediate is rounded to fp32, per
+# layer (the integer paths' 7-bit codes amplify such roundings)
+SPREAD = {"full_int8_packs2048": 0, "full_int4_packs2048": 0}
+SPREAD_FILE = os.path.join(HERE, "rounding_spread.npz")
+
+
+def write_spreads():
+    sys.path.insert(0, os.path.dirname(HERE))
+    from parity_bounds import rounding_spread  # composed from oracle functions only
+    arrays = {}
+    for name, pi in SPREAD.items():
+        t0 = time.time()
+        cfg = ti.workload(name)["cfg"]
+        w = ti.cached_storage_weights(cfg)
+        pack = ti.make_packs(name)[pi]
+        per_min, per_mean, fin_min, fin_mean = rounding_spread(cfg.as_dict(), w, pack.ids, pack.offsets)
+        key = f"{name}_pack{pi}"
+        arrays[key + "_min"] = per_min
+        arrays[key + "_mean"] = per_mean
+        arrays[key + "_final"] = np.array([fin_min, fin_mean])
+        arrays[key + "_fp"] = np.frombuffer(fingerprint(cfg, w, pack, None).encode(), np.uint8)
+        print(f"{name} pack {pi}: final 1-cos min {fin_min:.3e} mean {fin_mean:.3e} in {time.time() - t0:.1f}s",
+              flush=True)
+    np.savez(SPREAD_FILE, **arrays)
+
+
 def main(names):
+    if names == ["spread"]:
+        write_spreads()
+        return
     for name in names:
         arrays = {}
         for pi, texts in SELECTION[name]:
