@@ -14,14 +14,18 @@ synchronisation and measured on the host clock.
 
 Prints ONE JSON line: tokens/s (every token of every text, BOS/EOS included),
 the roofline of the dominant kernel, and the CPU oracle timed on a bounded
-sample of the same workload on the host's cores.  The roofline comes from a
-second timed pass of the same steps on a single stream with a HIP event pair
-around every launch of the dominant kernel on that stream (with several
-streams, kernels of different packs overlap and per-launch durations would
-include the time they share the chip).  An untimed single-stream step with
-event pairs around every launch adds the work rate of each kernel class
-("kernels": TFLOP/s and fraction of peak for the GEMMs and attention, GB/s
-for the row kernels).
+sample of the same workload on the host's cores.  An untimed single-stream
+step with an event pair around every launch gives each kernel class's time
+and work rate ("kernels": TFLOP/s and fraction of peak for the GEMMs and
+attention, GB/s for the row kernels); the dominant kernel is the one with
+the most time there (the two residual products, Wo and Wo2, are one kernel).
+Its roofline comes from a second timed pass of the same steps on a single
+stream with a HIP event pair recorded in the dispatch of every launch of
+that kernel (with several streams, kernels of different packs overlap and
+per-launch durations would include the time they share the chip).
+"configs" adds, from the same process, the other workloads: the fp32
+957-token pack, the 4 x 4096-token bf16 pack, the int8 and 4-bit pack
+streams (tokens/s and their own dominant kernel's fraction of peak).
 
 --row-kernels prints a different line instead: the HBM-bound row kernels
 (LayerNorm fp32 -> bf16 as in front of the bf16 products, and the per-row
@@ -47,6 +51,17 @@ DTYPE = {"bf16": "bf16", "fp32": "f32", "int8": "int8", "int4": "int8 (4-bit wei
 # flops per token of each GEMM class (H = 768, I = 3072): 2 * N * K
 GEMM_CLASSES = {"gemm_qkv": lambda H, I: 2 * 3 * H * H, "gemm_o": lambda H, I: 2 * H * H,
                 "gemm_geglu": lambda H, I: 2 * 2 * I * H, "gemm_o2": lambda H, I: 2 * H * I}
+
+
+# kernels by name -> the classes of tte_profile whose launches they run; the
+# residual products (Wo, Wo2) are one kernel template with the same tile
+KERNEL_GROUPS = {"k_gemm residual (Wo + Wo2)": ["gemm_o", "gemm_o2"], "k_gemm geglu (Wi)": ["gemm_geglu"],
+                 "k_gemm qkv": ["gemm_qkv"], "k_attn (global + local)": ["attn_global", "attn_local"],
+                 "k_ln": ["norm"], "k_quant7": ["quant"], "k_pool": ["pool"], "k_embed_ln": ["embed"]}
+GROUP_FILES = {"k_gemm residual (Wo + Wo2)": "kernels_gemm.hip", "k_gemm geglu (Wi)": "kernels_gemm.hip",
+               "k_gemm qkv": "kernels_gemm.hip", "k_attn (global + local)": "kernels_attn.hip"}
+GROUP_PROFILES = {"k_gemm residual (Wo + Wo2)": "traffic_gemm_resid_full_bf16_packs2048.json",
+                  "k_gemm geglu (Wi)": "traffic_gemm_geglu_full_bf16_packs2048.json"}
 
 
 def traffic_from_profile(kernel_source: str, profile: str):
@@ -173,8 +188,19 @@ def cpu_baseline(name, cfg, w, packs, budget_tokens):
         used += 1
     dt = time.perf_counter() - t0
     threads = max([i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()] or [1])
+    model = None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    # the oracle computes in fp64 by design (it is the reference the GPU
+    # paths are measured against); it is timed as it stands
     return {"value": round(n / dt, 2), "unit": "tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {used} packs ({n} tokens) of the workload, fp64 numpy, {dt:.1f}s"}
+            "sample": f"first {used} packs ({n} tokens) of the workload, fp64 numpy oracle as it stands, {dt:.1f}s",
+            "host_cpus": os.cpu_count(), "cpu_model": model, "blas_threads": threads}
 
 
 def main():
@@ -201,7 +227,9 @@ def main():
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-launch events of the dominant kernel")
     ap.add_argument("--no-breakdown", dest="breakdown", action="store_false",
-                    help="skip the untimed single-stream step that times every kernel class")
+                    help="leave the per-class kernel times of the untimed single-stream step out of the line")
+    ap.add_argument("--no-configs", dest="configs", action="store_false",
+                    help="skip the other workloads (fp32 957-token pack, 4 x 4096 bf16, int8 and 4-bit packs)")
     ap.add_argument("--row-kernels", action="store_true",
                     help="only measure the row kernels' HBM rate (LayerNorm, 7-bit quantisation) at two shapes")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -245,54 +273,159 @@ def main():
                           "value": big["GB/s"], "unit": "GB/s", "n_gpus": 1, "higher_is_better": True,
                           "peak": HBM_GBS, "data": "synthetic", "results": res}), flush=True)
         return
-    spec = ti.workload(a.workload)
-    cfg = spec["cfg"]
-    t0 = time.perf_counter()
-    w = ti.cached_storage_weights(cfg)
-    packs = ti.make_packs(a.workload)
-    cpu_packs = packs  # the CPU baseline always takes the workload's own packs
-    if a.merged:
-        # texts are independent: the whole step as one pack (one call)
-        packs = [ti.pack_from_texts([p.text(b) for p in packs for b in range(p.n_texts)])]
-        a.streams = 1
-    log(f"inputs ready in {time.perf_counter() - t0:.1f}s: {len(packs)} packs, "
-        f"{sum(p.n_tokens for p in packs)} tokens")
-    max_tokens = max(p.n_tokens for p in packs)
-    S = max(1, a.streams)
-    max_texts = max(1024, max(p.n_texts for p in packs))
-    max_len = max(512, max(int(np.diff(p.offsets).max()) for p in packs))
-    model = Model(cfg, w, max_tokens=max_tokens, max_text_len=max_len, max_texts=max_texts, device="cuda:0",
-                  split_k=a.split_k, graph=a.graph)
-    models = [model] + [Model(cfg, None, max_tokens=max_tokens, max_text_len=max_len, max_texts=max_texts,
-                              device="cuda:0", shared_from=model, split_k=a.split_k, graph=a.graph)
-                        for _ in range(S - 1)]
-    streams = [torch.cuda.Stream(device=dev) for _ in range(S)]
-    ids = [torch.from_numpy(p.ids).to(dev) for p in packs]
-    per_token = a.output == "tokens"
-    outs = [torch.empty((p.n_tokens if per_token else p.n_texts, cfg.hidden), dtype=torch.float32, device=dev)
-            for p in packs]
-    offs = [B.int32_array(p.offsets) for p in packs]
-    L = B.lib()
-    embed = L.tte_embed_tokens if per_token else L.tte_embed
+    runner = Runner(torch, ti, B, Model, a.workload, a.streams, merged=a.merged, per_token=a.output == "tokens",
+                    split_k=a.split_k, graph=a.graph, host_threads=a.host_threads)
+    runner.run_steps(a.warmup)
+    torch.cuda.synchronize()
+    log("warmup done")
+    secs = runner.timed(a.steps)
+    value = runner.tokens_per_step * a.steps / secs
+    log(f"timed {a.steps} steps on {runner.S} streams: {secs * 1e3:.2f} ms")
 
-    def step(n_streams):
-        for i, p in enumerate(packs):
-            k = i % n_streams
-            st = embed(models[k].handle, ids[i].data_ptr(), p.n_tokens, offs[i], p.n_texts, outs[i].data_ptr(),
-                       streams[k].cuda_stream)
-            if st != 0:
-                B.check(st)
+    # per-class kernel time of one untimed single-stream step; the dominant
+    # kernel is the one with the most time there
+    breakdown = runner.breakdown()
+    dominant = max((g for g in KERNEL_GROUPS if any(breakdown.get(c, {}).get("launches") for c in KERNEL_GROUPS[g])),
+                   key=lambda g: sum(breakdown.get(c, {}).get("ms", 0.0) for c in KERNEL_GROUPS[g]))
+    roofline, single_ms = None, None
+    if not a.no_kernel_events:
+        roofline, single_ms = runner.roofline(dominant, a.steps)
+        if roofline is not None and not a.merged and a.workload == "full_bf16_packs2048" and dominant in GROUP_PROFILES:
+            roofline["traffic"] = traffic_from_profile(
+                os.path.join(ROOT, "transformer_text_embedding_amd", "csrc", GROUP_FILES[dominant]),
+                os.path.join(ROOT, "profiles", GROUP_PROFILES[dominant]))
+    torch.cuda.synchronize()
+    cfg = runner.cfg
+    line = {
+        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": round(secs * 1e3 / a.steps, 3), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[cfg.precision], "data": "synthetic",
+        "config": {"workload": a.workload, "packs_per_step": len(runner.cpu_packs),
+                   "tokens_per_step": runner.tokens_per_step, "pack_budget": runner.spec.get("pack_budget"),
+                   "layers": cfg.layers, "hidden": cfg.hidden, "heads": cfg.heads, "intermediate": cfg.intermediate,
+                   "calls_per_step": len(runner.packs), "streams": runner.S,
+                   "hw_queues": int(os.environ.get("GPU_MAX_HW_QUEUES", "4")), "output": a.output,
+                   "split_k": a.split_k, "graph": a.graph, "merged": a.merged, "host_threads": a.host_threads,
+                   "single_stream_ms_per_step": round(single_ms, 3) if single_ms else None},
+        "roofline": roofline,
+    }
+    if a.breakdown:
+        line["kernels"] = public(breakdown)
+    cpu_w, cpu_packs = runner.w, runner.cpu_packs
+    runner.close()
+    if a.configs and a.workload == "full_bf16_packs2048" and not a.merged and a.output == "pooled":
+        line["configs"] = {}
+        for name, steps in SECONDARY:
+            log(f"config {name}")
+            r = Runner(torch, ti, B, Model, name, a.streams, host_threads=a.host_threads)
+            r.run_steps(1)
+            torch.cuda.synchronize()
+            sec = r.timed(steps)
+            bd = r.breakdown()
+            dom = max((g for g in KERNEL_GROUPS if any(bd.get(c, {}).get("launches") for c in KERNEL_GROUPS[g])),
+                      key=lambda g: sum(bd.get(c, {}).get("ms", 0.0) for c in KERNEL_GROUPS[g]))
+            line["configs"][name] = {
+                "tokens_per_s": round(r.tokens_per_step * steps / sec, 1), "ms_per_step": round(sec * 1e3 / steps, 3),
+                "steps": steps, "streams": r.S, "calls_per_step": len(r.packs), "tokens_per_step": r.tokens_per_step,
+                "dtype": DTYPE[r.cfg.precision], "dominant_kernel": dom, "dominant_frac_of_peak": group_frac(bd, dom),
+                "kernels": public(bd)}
+            r.close()
+            torch.cuda.empty_cache()
+    if not a.no_cpu_baseline:
+        log("timing the CPU oracle sample")
+        line["cpu_baseline"] = cpu_baseline(a.workload, cfg, cpu_w, cpu_packs, a.cpu_sample_tokens)
+    print(json.dumps(line), flush=True)
 
-    def run_steps(n_steps):
+
+# other workloads measured in the default run: (name, timed steps)
+SECONDARY = [("full_fp32_957", 30), ("full_bf16_4x4096", 10), ("full_int8_packs2048", 5),
+             ("full_int4_packs2048", 5)]
+
+
+def public(bd):
+    """A breakdown for the output line: the private work / peak fields
+    dropped."""
+    out = {k: {f: v for f, v in e.items() if not f.startswith("_")} for k, e in bd.items()}
+    out["measured_in"] = "untimed single-stream step, events in each launch's dispatch (pool: around its 2 kernels)"
+    return out
+
+
+def group_frac(bd, group):
+    """Fraction of peak of a kernel group from a breakdown: summed work over
+    summed time of its classes."""
+    present = [c for c in KERNEL_GROUPS[group] if c in bd and "_work" in bd[c]]
+    if not present:
+        return None
+    work = sum(bd[c]["_work"] for c in present)
+    ms = sum(bd[c]["ms"] for c in present)
+    unit_scale = 1e12 if "TFLOP/s" in bd[present[0]] else 1e9
+    return round(work / (ms / 1e3) / unit_scale / bd[present[0]]["_peak"], 4) if ms else None
+
+
+class Runner:
+    """One workload on S concurrent streams: one model (workspace) per stream
+    over one shared copy of the weights, packs dealt round-robin, one host
+    thread per stream enqueueing its packs (or all from this thread)."""
+
+    def __init__(self, torch, ti, B, Model, workload, streams, merged=False, per_token=False, split_k=False,
+                 graph=False, host_threads=True):
+        self.torch, self.B = torch, B
+        dev = torch.device("cuda:0")
+        self.spec = ti.workload(workload)
+        self.cfg = cfg = self.spec["cfg"]
+        t0 = time.perf_counter()
+        self.w = ti.cached_storage_weights(cfg)
+        packs = ti.make_packs(workload)
+        self.cpu_packs = packs  # the CPU baseline always takes the workload's own packs
+        if merged:
+            # texts are independent: the whole step as one pack (one call)
+            packs = [ti.pack_from_texts([p.text(b) for p in packs for b in range(p.n_texts)])]
+            streams = 1
+        self.packs = packs
+        log(f"{workload}: inputs ready in {time.perf_counter() - t0:.1f}s: {len(packs)} packs, "
+            f"{sum(p.n_tokens for p in packs)} tokens")
+        max_tokens = max(p.n_tokens for p in packs)
+        # a workload of one pack runs on one stream (its latency)
+        self.S = S = max(1, min(streams, len(packs)))
+        max_texts = max(1024, max(p.n_texts for p in packs))
+        max_len = max(512, max(int(np.diff(p.offsets).max()) for p in packs))
+        model = Model(cfg, self.w, max_tokens=max_tokens, max_text_len=max_len, max_texts=max_texts,
+                      device="cuda:0", split_k=split_k, graph=graph)
+        self.models = [model] + [Model(cfg, None, max_tokens=max_tokens, max_text_len=max_len, max_texts=max_texts,
+                                       device="cuda:0", shared_from=model, split_k=split_k, graph=graph)
+                                 for _ in range(S - 1)]
+        self.streams = [torch.cuda.Stream(device=dev) for _ in range(S)]
+        self.ids = [torch.from_numpy(p.ids).to(dev) for p in packs]
+        self.outs = [torch.empty((p.n_tokens if per_token else p.n_texts, cfg.hidden), dtype=torch.float32,
+                                 device=dev) for p in packs]
+        self.offs = [B.int32_array(p.offsets) for p in packs]
+        L = B.lib()
+        self.embed = L.tte_embed_tokens if per_token else L.tte_embed
+        self.host_threads = host_threads
+        self.tokens_per_step = sum(p.n_tokens for p in packs)
+
+    def call(self, i, k):
+        p = self.packs[i]
+        st = self.embed(self.models[k].handle, self.ids[i].data_ptr(), p.n_tokens, self.offs[i], p.n_texts,
+                        self.outs[i].data_ptr(), self.streams[k].cuda_stream)
+        if st != 0:
+            self.B.check(st)
+
+    def step(self, n_streams):
+        for i in range(len(self.packs)):
+            self.call(i, i % n_streams)
+
+    def run_steps(self, n_steps):
         """n_steps steps on S streams, from one host thread per stream:
         thread k enqueues packs k, k + S, ... of every step on stream k (the
         library calls release the interpreter lock, so the launches are
         issued in parallel; from one thread, the ~200 launches of each of
         the 64 packs limit the step at ~1.44M tokens/s); with
         --one-host-thread from this thread."""
-        if not a.host_threads or S == 1:
+        S = self.S
+        if not self.host_threads or S == 1:
             for _ in range(n_steps):
-                step(S)
+                self.step(S)
             return
         import threading
         errors = []
@@ -300,12 +433,8 @@ def main():
         def worker(k):
             try:
                 for _ in range(n_steps):
-                    for i in range(k, len(packs), S):
-                        p = packs[i]
-                        st = embed(models[k].handle, ids[i].data_ptr(), p.n_tokens, offs[i], p.n_texts,
-                                   outs[i].data_ptr(), streams[k].cuda_stream)
-                        if st != 0:
-                            B.check(st)
+                    for i in range(k, len(self.packs), S):
+                        self.call(i, k)
             except Exception as e:  # reported on the main thread
                 errors.append(e)
 
@@ -317,57 +446,26 @@ def main():
         if errors:
             raise errors[0]
 
-    torch.cuda.synchronize()
-    run_steps(a.warmup)
-    torch.cuda.synchronize()
-    log("warmup done")
-
-    tokens_per_step = sum(p.n_tokens for p in packs)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    run_steps(a.steps)
-    torch.cuda.synchronize()
-    secs = time.perf_counter() - t0
-    value = tokens_per_step * a.steps / secs
-    log(f"timed {a.steps} steps on {S} streams: {secs * 1e3:.2f} ms")
-
-    # single-stream pass: per-launch events around the dominant kernel
-    roofline = None
-    H, I = cfg.hidden, cfg.intermediate
-    dominant = "gemm_geglu"
-    single_ms = None
-    if not a.no_kernel_events:
-        h = models[0].handle
-        B.tte_profile_start(h, 1 << B.KERNEL_CLASSES.index(dominant), cfg.layers * len(packs) * a.steps + 16)
+    def timed(self, n_steps):
+        """Host seconds of n_steps steps between two device synchronisations."""
+        torch = self.torch
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(a.steps):
-            step(1)
+        self.run_steps(n_steps)
         torch.cuda.synchronize()
-        single_ms = (time.perf_counter() - t0) * 1e3 / a.steps
-        prof = B.tte_profile_stop(h)
-        ms_dom, n_dom = prof[dominant]
-        flops = GEMM_CLASSES[dominant](H, I) * tokens_per_step * cfg.layers * a.steps
-        achieved = flops / (ms_dom / 1e3) / 1e12
-        peak = PEAK_TFLOPS[cfg.precision]
-        traffic = None
-        if a.workload == "full_bf16_packs2048" and not a.merged:  # the counters' launch shapes
-            traffic = traffic_from_profile(
-                os.path.join(ROOT, "transformer_text_embedding_amd", "csrc", "kernels_gemm.hip"),
-                os.path.join(ROOT, "profiles", "traffic_gemm_geglu_full_bf16_packs2048.json"))
-        roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                    "frac": round(achieved / peak, 4), "traffic": traffic, "kernel": f"k_gemm ({dominant})",
-                    "launches": int(n_dom), "avg_launch_us": round(ms_dom * 1e3 / max(n_dom, 1), 2),
-                    "flops_per_launch_avg": int(flops / max(n_dom, 1)), "measured_in": "single-stream pass"}
+        return time.perf_counter() - t0
 
-    breakdown = None
-    if a.breakdown:
-        h = models[0].handle
-        B.tte_profile_start(h, (1 << B.TTE_K_COUNT) - 1, (10 * cfg.layers + 4) * len(packs) + 16)
-        step(1)
+    def breakdown(self):
+        """One untimed single-stream step with an event pair around every
+        launch: per class ms, launches and work rate (work and peak kept
+        under _work / _peak for group fractions, dropped from the output)."""
+        B = self.B
+        h = self.models[0].handle
+        B.tte_profile_start(h, (1 << B.TTE_K_COUNT) - 1, (10 * self.cfg.layers + 4) * len(self.packs) + 16)
+        self.step(1)
         prof = B.tte_profile_stop(h)
-        breakdown = {}
-        work = class_work(cfg, packs)
+        work = class_work(self.cfg, self.packs)
+        out = {}
         for k, (ms, n) in prof.items():
             if n == 0:
                 continue
@@ -381,32 +479,51 @@ def main():
                 else:
                     entry["GB/s"] = round(rate / 1e9, 1)
                     entry["frac_of_hbm"] = round(rate / 1e9 / HBM_GBS, 4)
-            breakdown[k] = entry
+                    peak = HBM_GBS
+                entry["_work"], entry["_peak"] = amount, peak
+            out[k] = entry
+        return out
 
-    torch.cuda.synchronize()
-    line = {
-        "metric": METRIC, "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
-        "warmup": a.warmup, "ms_per_step": round(secs * 1e3 / a.steps, 3), "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": DTYPE[cfg.precision], "data": "synthetic",
-        "config": {"workload": a.workload, "packs_per_step": len(cpu_packs), "tokens_per_step": tokens_per_step,
-                   "pack_budget": spec.get("pack_budget"), "layers": cfg.layers, "hidden": cfg.hidden,
-                   "heads": cfg.heads, "intermediate": cfg.intermediate, "calls_per_step": len(packs),
-                   "streams": S, "hw_queues": int(os.environ.get("GPU_MAX_HW_QUEUES", "4")), "output": a.output,
-                   "split_k": a.split_k, "graph": a.graph, "merged": a.merged, "host_threads": a.host_threads,
-                   "single_stream_ms_per_step": round(single_ms, 3) if single_ms else None},
-        "roofline": roofline,
-    }
-    if breakdown is not None:
-        # one pack at a time: the residual products' tiles are sized for
-        # packs on concurrent streams, so their lone rate here is low
-        breakdown["measured_in"] = "untimed single-stream step"
-        line["kernels"] = breakdown
-    if not a.no_cpu_baseline:
-        log("timing the CPU oracle sample")
-        line["cpu_baseline"] = cpu_baseline(a.workload, cfg, w, cpu_packs, a.cpu_sample_tokens)
-    for m in models:
-        m.close()
-    print(json.dumps(line), flush=True)
+    def roofline(self, group, n_steps):
+        """n_steps single-stream steps with an event pair in the dispatch of
+        every launch of the group's classes: its achieved rate against the
+        peak of its bound, and the step time on one stream."""
+        B, torch = self.B, self.torch
+        classes = KERNEL_GROUPS[group]
+        mask = 0
+        for c in classes:
+            mask |= 1 << B.KERNEL_CLASSES.index(c)
+        h = self.models[0].handle
+        B.tte_profile_start(h, mask, (len(classes) * self.cfg.layers + 4) * len(self.packs) * n_steps + 16)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_steps):
+            self.step(1)
+        torch.cuda.synchronize()
+        single_ms = (time.perf_counter() - t0) * 1e3 / n_steps
+        prof = B.tte_profile_stop(h)
+        work = class_work(self.cfg, self.packs)
+        ms = sum(prof[c][0] for c in classes)
+        n = sum(prof[c][1] for c in classes)
+        amount = sum(work[c][0] for c in classes if c in work) * n_steps
+        unit = work[classes[0]][1] if classes[0] in work else None
+        if not ms or unit is None:
+            return None, single_ms
+        if unit == "TFLOP/s":
+            achieved, peak, bound = amount / (ms / 1e3) / 1e12, work[classes[0]][2], "mfma"
+            per = {"flops_per_launch_avg": int(amount / max(n, 1))}
+        else:
+            achieved, peak, bound, unit = amount / (ms / 1e3) / 1e9, HBM_GBS, "hbm", "GB/s"
+            per = {"bytes_per_launch_avg": int(amount / max(n, 1))}
+        return ({"bound": bound, "achieved": round(achieved, 2), "peak": peak, "unit": unit,
+                 "frac": round(achieved / peak, 4), "traffic": None, "kernel": group, "classes": classes,
+                 "launches": int(n), "avg_launch_us": round(ms * 1e3 / max(n, 1), 2), **per,
+                 "measured_in": "single-stream pass, events in each launch's dispatch"}, single_ms)
+
+    def close(self):
+        for m in self.models:
+            m.close()
+        self.models = []
 
 
 if __name__ == "__main__":
