@@ -337,13 +337,17 @@ def test_full_size_integer_layers_from_the_gpus_own_states(full_models, name):
     its own.  Per token, the GPU's update of the residual stream (state
     after the layer minus before) against the oracle's.
 
-    Gates, from the CPU measurement of the same one-layer step with the
-    oracle's intermediates rounded to fp32 (half an ulp per value; int8 and
-    4-bit, every layer of this pack): 1 - cos of the update reaches at most
-    2.6e-4 on the worst token (a few codes flipped there) and 3.1e-7 averaged
-    over tokens.  The GPU's sums differ from the oracle's by a few fp32 ulps
-    rather than half of one, so proportionally more codes flip: the gates
-    allow mean <= 1e-5 and max <= 1e-2 per layer."""
+    What to expect, from the CPU measurement of the same one-layer step
+    with the oracle's intermediates rounded to fp32 (half an ulp per value;
+    int8 and 4-bit, every layer of this pack): a token whose path has no
+    flipped 7-bit code agrees to 1 - cos ~2e-14 (median and 99th percentile
+    <= 4.3e-14); fewer than 1% of tokens carry a flip, which moves them by up
+    to 2.6e-4.  The GPU's sums differ from the oracle's by a few fp32 ulps
+    rather than half of one, so more codes flip (its mean over tokens runs
+    ~10-50x the CPU's), but flips stay sparse.  A kernel mistake would move
+    most tokens.  Gates per layer: median token <= 1e-10 (any error common
+    to the tokens above ~1e-5 relative) and worst token <= 1e-2 (40x the
+    measured flip effect)."""
     cfg = ti.workload(name)["cfg"]
     w = ti.cached_storage_weights(cfg)
     pack = ti.make_packs(name)[0]
@@ -357,8 +361,10 @@ def test_full_size_integer_layers_from_the_gpus_own_states(full_models, name):
     for l in range(cfg.layers):
         ref = oracle.encoder_layer(c, w, l, got[l], pack.offsets)
         d = 1 - row_cosines(got[l + 1] - got[l], ref - got[l])
-        say(f"  layer {l:2d}: update 1-cos mean {d.mean():.3e} max {d.max():.3e}")
-        assert d.mean() <= 1e-5 and d.max() <= 1e-2, (l, d.mean(), d.max())
+        q50, q90, q99 = np.quantile(d, [0.5, 0.9, 0.99])
+        say(f"  layer {l:2d}: update 1-cos median {q50:.2e} p90 {q90:.2e} p99 {q99:.2e} max {d.max():.2e} "
+            f"mean {d.mean():.2e}; tokens > 1e-9: {np.mean(d > 1e-9) * 100:.1f}%")
+        assert q50 <= 1e-10 and d.max() <= 1e-2, (l, q50, d.max())
 
 
 def test_profile_counts_launches_and_leaves_results_alone():
