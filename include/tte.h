@@ -299,6 +299,22 @@ tte_status tte_op_qkv(tte_model* m, int32_t layer, const void* d_a, const float*
 tte_status tte_op_pool(tte_model* m, const float* d_x, int32_t n_tokens, const int32_t* h_offsets,
                        int32_t n_texts, float* d_out, void* stream);
 
+/* tte_op_pool with no device allocation and no workspace use, for callers
+ * that cannot allocate (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, validation, kernels and
+ * results (bit for bit) as tte_op_pool; the pack's offsets, pool-unit starts
+ * and per-unit partial sums go to a static device scratch of 8 MiB per GPU,
+ * held from the library's load until the process ends.  A pack needing more
+ * -- 8 * (n_texts + 1) bytes rounded up to 256, plus
+ * 4 * hidden * sum over texts of ceil(len / 32) -- is refused with
+ * TTE_E_UNSUPPORTED before anything is enqueued (hidden 768: about 2700
+ * partial rows, e.g. 85k tokens in long texts).  Every call on one GPU
+ * shares that scratch: calls that overlap on one GPU (other streams or
+ * threads) race and must be serialised by the caller; each call rewrites
+ * everything it reads, so nothing carries over between calls. */
+tte_status tte_op_pool_static(tte_model* m, const float* d_x, int32_t n_tokens, const int32_t* h_offsets,
+                              int32_t n_texts, float* d_out, void* stream);
+
 /* ---------------------------------------------------------------------------
  * Per-kernel timing with HIP events on the model's stream.
  * ------------------------------------------------------------------------- */

@@ -69,6 +69,7 @@ _SIGS = {
     "tte_op_qkv": (c_int32, [c_void_p, c_int32, c_void_p, c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p,
                              c_void_p, c_void_p]),
     "tte_op_pool": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p, c_void_p]),
+    "tte_op_pool_static": (c_int32, [c_void_p, c_void_p, c_int32, POINTER(c_int32), c_int32, c_void_p, c_void_p]),
     "tte_profile_start": (c_int32, [c_void_p, c_uint32, c_int32]),
     "tte_profile_stop": (c_int32, [c_void_p, POINTER(c_double), POINTER(c_int64)]),
     "tte_graph_stats": (c_int32, [c_void_p, POINTER(c_int32), POINTER(c_int32), POINTER(c_int64)]),
@@ -213,6 +214,12 @@ def tte_op_pool(model: int, d_x: int, n_tokens: int, offsets, d_out: int, stream
     arr = int32_array(offsets)
     check(lib().tte_op_pool(c_void_p(model), c_void_p(d_x), n_tokens, arr, len(offsets) - 1, c_void_p(d_out),
                             c_void_p(stream)))
+
+
+def tte_op_pool_static(model: int, d_x: int, n_tokens: int, offsets, d_out: int, stream: int) -> None:
+    arr = int32_array(offsets)
+    check(lib().tte_op_pool_static(c_void_p(model), c_void_p(d_x), n_tokens, arr, len(offsets) - 1, c_void_p(d_out),
+                                   c_void_p(stream)))
 
 
 def tte_profile_start(model: int, class_mask: int, max_launches: int) -> None:

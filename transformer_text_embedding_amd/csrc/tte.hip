@@ -13,6 +13,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -489,6 +490,71 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
   return hip_check(hipGetLastError(), "kernel launch");
 }
 
+// --------------------------------------------------------------------------
+// Allocation-free pooling (tte_op_pool_static): its scratch -- the pack's
+// offsets and pool-unit starts, then the per-unit partial sums -- lives in a
+// file-scope device array that each GPU holds from the library's load until
+// the process ends.  In host code `scratch` names a host-side stand-in, not
+// device memory: every host use goes through the address hipGetSymbolAddress
+// returns for the current device (scratch_on), never the array's name.
+// --------------------------------------------------------------------------
+
+constexpr size_t STATIC_SCRATCH_BYTES = size_t(8) << 20;  // 8 MiB per GPU
+constexpr int STATIC_SCRATCH_DEVICES = 64;
+
+}  // namespace
+
+static __device__ __align__(256) uint8_t scratch[STATIC_SCRATCH_BYTES];
+
+namespace {
+
+std::once_flag g_scratch_once[STATIC_SCRATCH_DEVICES];
+uint8_t* g_scratch_ptr[STATIC_SCRATCH_DEVICES];
+hipError_t g_scratch_err[STATIC_SCRATCH_DEVICES];
+
+// Device address of `scratch` on `device`, looked up once per device; the
+// caller has made `device` current (each GPU holds its own copy of the array
+// at its own address).
+tte_status scratch_on(int device, uint8_t** out) {
+  if (device < 0 || device >= STATIC_SCRATCH_DEVICES)
+    return fail(TTE_E_UNSUPPORTED, "static scratch: device index above 63");
+  std::call_once(g_scratch_once[device], [device] {
+    void* p = nullptr;
+    g_scratch_err[device] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[device] = reinterpret_cast<uint8_t*>(p);
+  });
+  if (g_scratch_err[device] != hipSuccess || !g_scratch_ptr[device])
+    return fail(TTE_E_DEVICE, std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(g_scratch_err[device]));
+  *out = g_scratch_ptr[device];
+  return TTE_OK;
+}
+
+// Offsets and pool-unit starts of a pack, copied to d_dst through the
+// model's pinned staging ring (one stream-ordered copy).
+tte_status stage_offsets_to(tte_model* m, const int32_t* h_off, int n_texts, int n_units, void* d_dst,
+                            hipStream_t s) {
+  const int slot = m->stage_next;
+  m->stage_next = (slot + 1) % STAGE_SLOTS;
+  if (m->stage_pending[slot]) {
+    tte_status st = hip_check(hipEventSynchronize(m->stage_ev[slot]), "hipEventSynchronize");
+    if (st != TTE_OK) return st;
+    m->stage_pending[slot] = false;
+  }
+  int* so = m->h_stage + (size_t)slot * stage_ints(m->cfg);
+  int* su = so + (n_texts + 1);
+  std::memcpy(so, h_off, sizeof(int) * (size_t)(n_texts + 1));
+  su[0] = 0;
+  for (int b = 0; b < n_texts; ++b) su[b + 1] = su[b] + (h_off[b + 1] - h_off[b] + POOL_ROWS - 1) / POOL_ROWS;
+  (void)n_units;
+  tte_status st = hip_check(hipMemcpyAsync(d_dst, so, sizeof(int) * 2 * (size_t)(n_texts + 1), hipMemcpyHostToDevice, s),
+                            "hipMemcpyAsync(offsets)");
+  if (st != TTE_OK) return st;
+  st = hip_check(hipEventRecord(m->stage_ev[slot], s), "hipEventRecord");
+  if (st != TTE_OK) return st;
+  m->stage_pending[slot] = true;
+  return TTE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -800,6 +866,39 @@ tte_status tte_op_pool(tte_model* m, const float* d_x, int32_t n_tokens, const i
   if (st != TTE_OK) return st;
   launch_pool(d_x, m->w.final_norm, m->cfg.ln_eps, m->cfg.hidden, m->d_off, m->d_unit, n_texts, n_units, m->partial,
               d_out, s);
+  return hip_check(hipGetLastError(), "kernel launch");
+}
+
+tte_status tte_op_pool_static(tte_model* m, const float* d_x, int32_t n_tokens, const int32_t* h_offsets,
+                              int32_t n_texts, float* d_out, void* stream) {
+  if (!m) return fail(TTE_E_INVALID, "model is NULL");
+  tte_status st = check_pack(m->cfg, n_tokens, h_offsets, n_texts);
+  if (st != TTE_OK) return st;
+  if (n_texts == 0) return TTE_OK;
+  if (!d_x || !d_out) return fail(TTE_E_INVALID, "NULL buffer");
+  const int H = m->cfg.hidden;
+  int64_t n_units = 0;
+  for (int b = 0; b < n_texts; ++b) n_units += (h_offsets[b + 1] - h_offsets[b] + POOL_ROWS - 1) / POOL_ROWS;
+  // layout: offsets [n_texts + 1], unit starts [n_texts + 1], then (256-byte
+  // aligned) the partial sums [n_units, H] fp32
+  const size_t head = al(sizeof(int) * 2 * ((size_t)n_texts + 1));
+  const size_t need = head + (size_t)n_units * H * 4;
+  if (need > STATIC_SCRATCH_BYTES)
+    return fail(TTE_E_UNSUPPORTED, "tte_op_pool_static: the pack needs " + std::to_string(need) +
+                                       " bytes of scratch (offsets + ceil(len/32) partial rows of hidden fp32 per "
+                                       "text); the static scratch holds " + std::to_string(STATIC_SCRATCH_BYTES));
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  st = hip_check(hipSetDevice(m->device), "hipSetDevice");
+  if (st != TTE_OK) return st;
+  uint8_t* base = nullptr;
+  st = scratch_on(m->device, &base);
+  if (st != TTE_OK) return st;
+  (void)hipGetLastError();
+  int* d_off = reinterpret_cast<int*>(base);
+  st = stage_offsets_to(m, h_offsets, n_texts, (int)n_units, d_off, s);
+  if (st != TTE_OK) return st;
+  launch_pool(d_x, m->w.final_norm, m->cfg.ln_eps, H, d_off, d_off + (n_texts + 1), n_texts, (int)n_units,
+              reinterpret_cast<float*>(base + head), d_out, s);
   return hip_check(hipGetLastError(), "kernel launch");
 }
 
