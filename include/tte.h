@@ -69,13 +69,14 @@ typedef enum {
 
 /* Execution options (tte_config.flags). */
 typedef enum {
-  /* Split the down-projection (I -> H) of short packs over K into two
-   * partial products, summed into the residual stream by the next norm
-   * kernel.  A 768-wide output of a ~2k-token pack makes fewer tiles than
-   * the chip has compute units; splitting doubles them and shortens one
-   * call by about 5%.  It costs 2 * max_tokens * H * 4 bytes of workspace
-   * and extra HBM traffic, which lowers throughput when several calls
-   * already share the GPU on concurrent streams, so it is off by default. */
+  /* Split the two residual products (attention output H -> H and the
+   * down-projection I -> H) of short packs over K into up to four partial
+   * products, summed into the residual stream, in part order, by the norm
+   * kernel that follows each.  An H-wide output of a ~2k-token pack makes
+   * fewer tiles than the chip's compute units can hold; the parts fill
+   * them (the count is chosen per product from its shape, so it is the
+   * same for every call of a shape).  Costs 4 * max_tokens * H * 4 bytes
+   * of workspace and the partials' memory traffic. */
   TTE_FLAG_SPLIT_K = 1,
   /* HIP-graph replay of the pass.  Prior art: the xujun.org note on 58.com's
    * multimodal (VLM) inference optimisation, section 4.3 (CUDA graphs for

@@ -44,7 +44,7 @@ def test_workspace_size_grows_with_limits(lib):
 def test_split_k_flag_adds_partials_workspace(lib):
     a = B.tte_workspace_size(_cfg())
     b = B.tte_workspace_size(_cfg(flags=B.TTE_FLAG_SPLIT_K))
-    assert b - a == 2 * 2048 * 768 * 4  # two fp32 partial products [max_tokens, H]
+    assert b - a == 4 * 2048 * 768 * 4  # up to four fp32 partial products [max_tokens, H]
 
 
 def test_graph_stats_rejects_null(lib):

@@ -10,7 +10,9 @@ import re
 from ctypes import POINTER, c_char_p, c_double, c_float, c_int8, c_int32, c_int64, c_size_t, c_uint32, c_void_p
 
 PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG, "libtte.so")
+# TTE_LIBRARY: path of another build of the library (e.g. a variant to
+# compare against); the package's own libtte.so otherwise
+LIB_PATH = os.environ.get("TTE_LIBRARY") or os.path.join(PKG, "libtte.so")
 HEADER = os.path.join(os.path.dirname(PKG), "include", "tte.h")
 
 TTE_OK, TTE_E_INVALID, TTE_E_UNSUPPORTED, TTE_E_NOMEM, TTE_E_DEVICE = range(5)

@@ -106,6 +106,11 @@ void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const v
 void launch_gemm_splitk(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
                         int N, int K, int splits, float* partials, hipStream_t s);
 
+// Number of K parts (1 .. max_splits) for a residual product M x N x K
+// run split (launch_gemm_splitk): enough to fill two blocks per compute
+// unit, each part at least 6 K tiles.
+int residual_splits(int prec, int M, int N, int K, int max_splits);
+
 // x += partials[0] + ... + partials[splits-1] (in that order), then the
 // bias-free LayerNorm (gamma non-null) or plain conversion (gamma null) of
 // the new x to out (fp32 / bf16 / 7-bit codes + scales), or no output
@@ -126,9 +131,14 @@ void launch_qkv_prep(int prec, const void* qkv_in, void* qk_out, const QkvOut& q
 // Attention over the packed axis.  qk: [T, 3H] with rotated Q and K in
 // columns 0 .. 2H-1; vt: V transposed [H][vt_stride]; o: [T, H].  fp32 or
 // bf16 operands.  mean_len: the pack's mean text length (tokens), which
-// picks the query block size.
+// picks the query block size.  d_off / d_qunit (device, n_texts + 1 each):
+// the offsets and the starts of each text's units of ATTN_QUNIT queries
+// (prefix sums of ceil(len / ATTN_QUNIT)); with them the 64-query blocks
+// are text-aligned units, without them BQ consecutive queries of the pack.
+constexpr int ATTN_QUNIT = 64;
 void launch_attention(int prec, const void* qk, const void* vt, int vt_stride, void* o, const Seg* seg, int T,
-                      int n_heads, int is_global, int window, int mean_len, hipStream_t s);
+                      int n_heads, int is_global, int window, int mean_len, hipStream_t s, const int* d_off = nullptr,
+                      const int* d_qunit = nullptr, int n_texts = 0);
 
 // Cosine-similarity matrix of unit vectors: sim [n, n] = E E^T, E fp32
 // [n, dim] row-major, dim % 16 == 0.

@@ -162,10 +162,10 @@ __device__ __forceinline__ long unpack_q4(uint32_t x) {
 }
 
 template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES, int WGM, int WGN, int KT>
-// The 128 x 192 bf16 GeGLU tiles (WN = 6) are held to 4 waves per SIMD, 128
-// registers, so that two blocks share a CU (the compiler spills two
-// registers for it); every other shape takes what it needs.
-__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WN == 6 ? 4 : 1))) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
+// The 128 x 192 bf16 GeGLU tiles (32 x 96 waves) are held to 4 waves per
+// SIMD, 128 registers, so that two blocks share a CU (the compiler spills
+// two registers for it); every other shape takes what it needs.
+__global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(WN == 6 && WM == 2 ? 4 : 1))) void k_gemm(const uint8_t* __restrict__ A, const float* __restrict__ a_scale,
                                               const uint8_t* __restrict__ W, const float* __restrict__ w_scale,
                                               void* __restrict__ C, int M, int N, int K, int n_blocks,
                                               int m_blocks, int grp, int splits, QkvOut qo) {
@@ -719,7 +719,15 @@ TileCfg pick_tiles(int prec, int epi, int M, int n_cols, int K) {
 template <int PREC>
 void launch_prec(int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N,
                  int K, void* C, int out_kind, hipStream_t s) {
-  switch (pick_tiles(PREC, epi, M, epi == E_GEGLU ? 2 * N : N, K)) {
+  // Tiles that run a lone product faster measured slower in the pass with
+  // packs on four concurrent streams, which shares the chip between them
+  // (interleaved runs, tokens/s): residual products in 128 x 64 tiles of 3
+  // stages (alone: down-projection 26.0 against 35.0 us) 1.37M against
+  // 1.43M, with GeGLU also in 128 x 192 tiles 1.36M, residual in 64 x 64
+  // tiles 1.30M.  The 90 large residual blocks of a ~2k-token pack leave
+  // most compute units to the other streams' kernels.
+  const TileCfg tc = pick_tiles(PREC, epi, M, epi == E_GEGLU ? 2 * N : N, K);
+  switch (tc) {
     case T128: go_prec<PREC, 4, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
     case T32: go_prec<PREC, 1, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
     case T64L: go_prec<PREC, 2, 3>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
@@ -771,23 +779,44 @@ void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const v
   else launch_prec<P_I4>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
 }
 
+int residual_splits(int prec, int M, int N, int K, int max_splits) {
+  // 96 x 128 tiles of 4 waves take ~56 KB of LDS at two stages, so two
+  // blocks share a CU: a product of fewer tiles than the 512 such slots
+  // leaves compute units idle, and cutting K into parts fills them.  Each
+  // part keeps >= 6 K tiles (the pipeline's fill is paid per part).
+  // Measured on MI355X, bf16, back to back: the down-projection of a
+  // 1913-token pack (N 768, K 3072) 35.0 us unsplit in 128 x 128 tiles,
+  // 18.5 in two parts, 16.3 in three, 14.5 in four; the attention output
+  // product (K 768) 7.7 unsplit in 128 x 64 tiles, 7.3 in two parts.
+  if (M <= 0 || N % 128 != 0) return 1;
+  const int bk = 128 / (prec == P_F32 ? 4 : prec == P_BF16 ? 2 : 1);  // K elements per tile
+  if (K % bk != 0) return 1;
+  const long tiles = (long)((M + 95) / 96) * (N / 128);
+  const int nk = K / bk;
+  int best = 1;
+  for (int sp = 2; sp <= max_splits; ++sp)
+    if (nk % sp == 0 && nk / sp >= 6 && tiles * sp <= 512) best = sp;
+  return best;
+}
+
 void launch_gemm_splitk(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
                         int N, int K, int splits, float* partials, hipStream_t s) {
   if (M <= 0) return;
-  // 64 x 128 tiles; a third stage when each part is long
+  // 96 x 128 tiles of 4 waves (48 x 64 each); a third stage when each part
+  // is long
   const bool long_k = K / splits > 1024;
   if (prec == P_F32) {
-    if (long_k) go<P_F32, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
-    else go<P_F32, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    if (long_k) go<P_F32, E_PART, O_F32, 3, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    else go<P_F32, E_PART, O_F32, 3, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
   } else if (prec == P_BF16) {
-    if (long_k) go<P_BF16, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
-    else go<P_BF16, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    if (long_k) go<P_BF16, E_PART, O_F32, 3, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    else go<P_BF16, E_PART, O_F32, 3, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
   } else if (prec == P_I8) {
-    if (long_k) go<P_I8, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
-    else go<P_I8, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    if (long_k) go<P_I8, E_PART, O_F32, 3, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    else go<P_I8, E_PART, O_F32, 3, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
   } else {
-    if (long_k) go<P_I4, E_PART, O_F32, 2, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
-    else go<P_I4, E_PART, O_F32, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    if (long_k) go<P_I4, E_PART, O_F32, 3, 4, 3>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
+    else go<P_I4, E_PART, O_F32, 3, 4, 2>(A, a_scale, W, w_scale, M, N, K, partials, s, QkvOut{}, splits);
   }
 }
 

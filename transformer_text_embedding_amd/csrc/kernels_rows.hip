@@ -217,11 +217,18 @@ __global__ __launch_bounds__(256) void k_resid_ln(float* __restrict__ x, const f
   if (r >= rows) return;
   float v[EPL];
   load_f32_row<EPL>(x + (size_t)r * Wd, lane, v);
-  for (int sp = 0; sp < splits; ++sp) {
-    float p[EPL];
-    load_f32_row<EPL>(partials + ((size_t)sp * rows + r) * Wd, lane, p);
+  // up to 4 partial rows in flight at once, added in split order
+  for (int sp0 = 0; sp0 < splits; sp0 += 4) {
+    float p[4][EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) v[i] += p[i];
+    for (int j = 0; j < 4; ++j)
+      if (sp0 + j < splits) load_f32_row<EPL>(partials + ((size_t)(sp0 + j) * rows + r) * Wd, lane, p[j]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (sp0 + j < splits) {
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) v[i] += p[j][i];
+      }
   }
   store_f32_row<EPL>(x + (size_t)r * Wd, lane, v);
   if constexpr (WRITE) {

@@ -33,6 +33,9 @@ tte_status fail(tte_status s, const std::string& msg) {
 
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
+// most K parts of a split residual product (TTE_FLAG_SPLIT_K)
+constexpr int MAX_SPLITS = 4;
+
 struct Layout {
   size_t x, xa, ascale, qkv, vt, o, y, kpart, seg, off, partial, cosg, sing, cosl, sinl, total;
   int max_units;
@@ -62,10 +65,12 @@ Layout layout_of(const tte_config& c) {
   L.vt = take(H * (size_t)L.vt_stride * ab);
   L.o = take(T * H * ab);
   L.y = take(T * I * ab);
-  L.kpart = take(c.flags & TTE_FLAG_SPLIT_K ? 2 * T * H * 4 : 0);  // split-K partials of the down-projection
+  // split-K partials of the residual products
+  L.kpart = take(c.flags & TTE_FLAG_SPLIT_K ? (size_t)MAX_SPLITS * T * H * 4 : 0);
   L.seg = take(T * sizeof(Seg));
-  // the call's PackIO, then its offsets and pool-unit starts back to back
-  L.off = take(sizeof(PackIO) + 2 * ((size_t)c.max_texts + 1) * 4);
+  // the call's PackIO, then its offsets, pool-unit starts and attention
+  // query-unit starts back to back
+  L.off = take(sizeof(PackIO) + 3 * ((size_t)c.max_texts + 1) * 4);
   L.partial = take((size_t)L.max_units * H * 4);
   const size_t rope = (size_t)c.max_text_len * 32 * 4;
   L.cosg = take(rope);
@@ -154,6 +159,7 @@ struct tte_model {
   PackIO* d_io;  // the call's ids / output pointers (read by graph replays)
   int* d_off;
   int* d_unit;   // d_off + n_texts + 1 of the last upload
+  int* d_qunit;  // d_off + 2 (n_texts + 1): starts of each text's 64-query attention units
   float* partial;
   const float *cosg, *sing, *cosl, *sinl;
   // pinned staging for the per-call offsets upload: a ring of slots, each
@@ -230,7 +236,7 @@ tte_status hip_check(hipError_t e, const char* what) {
 // only once the previous copy from it is done.  Sets m->d_unit.
 constexpr int STAGE_SLOTS = 8;
 
-size_t stage_ints(const tte_config& c) { return sizeof(PackIO) / 4 + 2 * ((size_t)c.max_texts + 1); }
+size_t stage_ints(const tte_config& c) { return sizeof(PackIO) / 4 + 3 * ((size_t)c.max_texts + 1); }
 
 tte_status upload_pack(tte_model* m, const int32_t* h_off, int n_texts, int* n_units, hipStream_t s,
                        const int32_t* d_ids = nullptr, float* d_out = nullptr) {
@@ -246,12 +252,19 @@ tte_status upload_pack(tte_model* m, const int32_t* h_off, int n_texts, int* n_u
   std::memcpy(base, &io, sizeof(PackIO));
   int* so = base + sizeof(PackIO) / 4;
   int* su = so + (n_texts + 1);
+  int* sq = su + (n_texts + 1);
   std::memcpy(so, h_off, sizeof(int) * (size_t)(n_texts + 1));
   su[0] = 0;
-  for (int b = 0; b < n_texts; ++b) su[b + 1] = su[b] + (h_off[b + 1] - h_off[b] + POOL_ROWS - 1) / POOL_ROWS;
+  sq[0] = 0;
+  for (int b = 0; b < n_texts; ++b) {
+    const int len = h_off[b + 1] - h_off[b];
+    su[b + 1] = su[b] + (len + POOL_ROWS - 1) / POOL_ROWS;
+    sq[b + 1] = sq[b] + (len + ATTN_QUNIT - 1) / ATTN_QUNIT;
+  }
   *n_units = su[n_texts];
   m->d_unit = m->d_off + (n_texts + 1);
-  const size_t bytes = sizeof(PackIO) + sizeof(int) * 2 * (size_t)(n_texts + 1);
+  m->d_qunit = m->d_off + 2 * (n_texts + 1);
+  const size_t bytes = sizeof(PackIO) + sizeof(int) * 3 * (size_t)(n_texts + 1);
   tte_status st = hip_check(hipMemcpyAsync(m->d_io, base, bytes, hipMemcpyHostToDevice, s), "hipMemcpyAsync(offsets)");
   if (st != TTE_OK) return st;
   st = hip_check(hipEventRecord(m->stage_ev[slot], s), "hipEventRecord");
@@ -302,12 +315,13 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
   }
   if (d_states) (void)hipMemcpyAsync(d_states, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
 
-  // With TTE_FLAG_SPLIT_K the down-projection of a short pack runs split-K
-  // (its H-wide output gives fewer 64 x 128 tiles than there are compute
-  // units); its two partial products are added to the residual stream by the
-  // next norm kernel.
-  const int o2_splits =
-      ((c.flags & TTE_FLAG_SPLIT_K) && I >= 2048 && ((T + 63) / 64) * (H / 128) < 256) ? 2 : 1;
+  // With TTE_FLAG_SPLIT_K the residual products of a short pack run split-K
+  // (their H-wide outputs give fewer tiles than the compute units can hold);
+  // the partial products are added to the residual stream, in part order,
+  // by the next norm kernel.
+  const bool split = (c.flags & TTE_FLAG_SPLIT_K) != 0;
+  const int o_splits = split ? residual_splits(P, T, H, H, MAX_SPLITS) : 1;
+  const int o2_splits = split ? residual_splits(P, T, H, I, MAX_SPLITS) : 1;
   bool pending = false;  // x still lacks the partials of the last down-projection
   const bool integer = P == TTE_INT8 || P == TTE_INT4;  // 7-bit activation codes into the weight products
   const int in_fmt = integer ? O_I8 : act;
@@ -334,7 +348,7 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
     {
       ProfScope ps(m, glob ? TTE_K_ATTN_GLOBAL : TTE_K_ATTN_LOCAL, s);
       launch_attention(P == TTE_BF16 ? P_BF16 : P_F32, m->qkv, m->vt, m->L.vt_stride, m->o, m->seg, T, nh, glob,
-                       c.window, T / B, s);
+                       c.window, T / B, s, m->d_off, m->d_qunit, B);
     }
     const void* o_in = m->o;
     if (integer) {
@@ -344,11 +358,14 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
     }
     {
       ProfScope ps(m, TTE_K_GEMM_O, s);
-      launch_gemm(P, E_RESID, o_in, m->ascale, LW.wo, LW.wo_scale, T, H, H, m->x, O_F32, s);
+      if (o_splits > 1) launch_gemm_splitk(P, o_in, m->ascale, LW.wo, LW.wo_scale, T, H, H, o_splits, m->kpart, s);
+      else launch_gemm(P, E_RESID, o_in, m->ascale, LW.wo, LW.wo_scale, T, H, H, m->x, O_F32, s);
     }
     {
       ProfScope ps(m, TTE_K_NORM, s);
-      launch_ln(m->x, LW.mlp_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
+      if (o_splits > 1)
+        launch_resid_ln(m->x, m->kpart, o_splits, LW.mlp_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
+      else launch_ln(m->x, LW.mlp_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
     }
     {
       ProfScope ps(m, TTE_K_GEMM_GEGLU, s);
@@ -624,6 +641,7 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   m->d_io = reinterpret_cast<PackIO*>(b + L.off);
   m->d_off = reinterpret_cast<int*>(b + L.off + sizeof(PackIO));
   m->d_unit = m->d_off + 1;
+  m->d_qunit = m->d_off + 2;
   m->partial = reinterpret_cast<float*>(b + L.partial);
   m->cosg = reinterpret_cast<const float*>(b + L.cosg);
   m->sing = reinterpret_cast<const float*>(b + L.sing);
@@ -814,7 +832,7 @@ tte_status tte_op_attention(tte_model* m, int32_t layer, const void* d_qkv, int3
   const QkvOut qo{m->seg, glob ? m->cosg : m->cosl, glob ? m->sing : m->sinl, m->vt, m->L.vt_stride, m->cfg.hidden};
   launch_qkv_prep(prec, d_qkv, m->qkv, qo, n_tokens, s);
   launch_attention(prec, m->qkv, m->vt, m->L.vt_stride, d_o, m->seg, n_tokens, m->cfg.n_heads, glob, m->cfg.window,
-                   n_tokens / n_texts, s);
+                   n_tokens / n_texts, s, m->d_off, m->d_qunit, n_texts);
   return hip_check(hipGetLastError(), "kernel launch");
 }
 
