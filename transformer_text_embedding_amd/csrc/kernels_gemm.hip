@@ -425,26 +425,61 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x4f32((float)s_blk[mt], neg_eo, acc[mt][nt], 0, 0, 0);
       }
     } else {
+      // int8: per 32-input block c, one MFMA per output tile gives the exact
+      // int32 block sum P, then acc += float(P) * w_scale[n, c] on the VALU
+      // (4 cvt + 4 FMA per MFMA).  Two-block software pipeline: block c + 1's
+      // MFMAs go into their own registers while block c's sums are scaled,
+      // so the VALU work overlaps the matrix cores instead of waiting for
+      // each MFMA's result in turn.  Each accumulator still adds its blocks
+      // in order 0 .. 3, as before.
       const float* sc = reinterpret_cast<const float*>(stage + G::AREG + G::WREG);
       f32x4 sw[WN];
 #pragma unroll
       for (int nt = 0; nt < WN; ++nt) sw[nt] = *reinterpret_cast<const f32x4*>(sc + 4 * (wn * 16 * WN + nt * 16 + li));
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
+      long af[2][WM], bf[2][WN];
+      i32x4 pb[2][WM][WN];
+      auto read_blk = [&](int c, long* a, long* b) {
         const int off = (((2 * c + (g >> 1)) ^ swz) << 4) + ((g & 1) << 3);
-        long af[WM], bf[WN];
 #pragma unroll
-        for (int t = 0; t < WM; ++t) af[t] = *reinterpret_cast<const long*>(As + t * 16 * ROW + off);
+        for (int t = 0; t < WM; ++t) a[t] = *reinterpret_cast<const long*>(As + t * 16 * ROW + off);
 #pragma unroll
-        for (int t = 0; t < WN; ++t) bf[t] = *reinterpret_cast<const long*>(Bs + t * 16 * ROW + off);
+        for (int t = 0; t < WN; ++t) b[t] = *reinterpret_cast<const long*>(Bs + t * 16 * ROW + off);
+      };
+      auto mfma_blk = [&](const long* a, const long* b, i32x4 (&pp)[WM][WN]) {
 #pragma unroll
         for (int mt = 0; mt < WM; ++mt)
 #pragma unroll
-          for (int nt = 0; nt < WN; ++nt) {
-            const i32x4 p = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[mt], bf[nt], i32x4{0, 0, 0, 0}, 0, 0, 0);
+          for (int nt = 0; nt < WN; ++nt)
+            pp[mt][nt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[mt], b[nt], i32x4{0, 0, 0, 0}, 0, 0, 0);
+      };
+      auto scale_one = [&](const i32x4& pp, f32x4& a, float s_) {
 #pragma unroll
-            for (int r = 0; r < 4; ++r) acc[mt][nt][r] = __builtin_fmaf((float)p[r], sw[nt][c], acc[mt][nt][r]);
-          }
+        for (int r = 0; r < 4; ++r) a[r] = __builtin_fmaf((float)pp[r], s_, a[r]);
+      };
+      read_blk(0, af[0], bf[0]);
+      mfma_blk(af[0], bf[0], pb[0]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int cur = c & 1, nxt = cur ^ 1;
+        if (c + 1 < 4) {
+          read_blk(c + 1, af[nxt], bf[nxt]);
+          // pairs (block c + 1's MFMA of tile i, block c's scaling of tile
+          // i), kept in this order by scheduling barriers: the VALU reads a
+          // sum produced WM * WN MFMAs earlier, so neither unit waits
+#pragma unroll
+          for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < WN; ++nt) {
+              pb[nxt][mt][nt] = __builtin_amdgcn_mfma_i32_16x16x32_i8(af[nxt][mt], bf[nxt][nt], i32x4{0, 0, 0, 0}, 0, 0, 0);
+              scale_one(pb[cur][mt][nt], acc[mt][nt], sw[nt][c]);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < WM; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < WN; ++nt) scale_one(pb[cur][mt][nt], acc[mt][nt], sw[nt][c]);
+        }
       }
     }
   }
