@@ -318,7 +318,7 @@ def main():
         for name, steps in SECONDARY:
             log(f"config {name}")
             r = Runner(torch, ti, B, Model, name, a.streams, host_threads=a.host_threads)
-            r.run_steps(1)
+            r.run_steps(2)
             torch.cuda.synchronize()
             sec = r.timed(steps)
             bd = r.breakdown()
@@ -326,7 +326,7 @@ def main():
                       key=lambda g: sum(bd.get(c, {}).get("ms", 0.0) for c in KERNEL_GROUPS[g]))
             line["configs"][name] = {
                 "tokens_per_s": round(r.tokens_per_step * steps / sec, 1), "ms_per_step": round(sec * 1e3 / steps, 3),
-                "steps": steps, "streams": r.S, "calls_per_step": len(r.packs), "tokens_per_step": r.tokens_per_step,
+                "steps": steps, "warmup": 2, "streams": r.S, "calls_per_step": len(r.packs), "tokens_per_step": r.tokens_per_step,
                 "dtype": DTYPE[r.cfg.precision], "dominant_kernel": dom, "dominant_frac_of_peak": group_frac(bd, dom),
                 "kernels": public(bd)}
             r.close()
@@ -338,8 +338,8 @@ def main():
 
 
 # other workloads measured in the default run: (name, timed steps)
-SECONDARY = [("full_fp32_957", 30), ("full_bf16_4x4096", 10), ("full_int8_packs2048", 5),
-             ("full_int4_packs2048", 5)]
+SECONDARY = [("full_fp32_957", 30), ("full_bf16_4x4096", 10), ("full_int8_packs2048", 10),
+             ("full_int4_packs2048", 10)]
 
 
 def public(bd):
