@@ -261,7 +261,10 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
 #if TTE_BF16_PIPE
   // (two-stage rings only: with a third stage the later load issue of this
   // scheme measured slower for the long-K down-projection)
-  if constexpr (PREC == P_BF16 && G::STAGES == 2) {
+  // The residual products (N = hidden, few tiles per pack) run the plain
+  // loop below: with four packs in flight the fragment-ahead form was
+  // ~1% slower for them, while it stays ahead for the wider products.
+  if constexpr (PREC == P_BF16 && G::STAGES == 2 && EPI != E_RESID) {
     // Fragment reads one 32-wide k-step ahead of the MFMAs, across the
     // barrier: the last k-step's MFMAs of tile kt run while the first
     // k-step's fragments of tile kt+1 come from LDS.  The barrier sits
