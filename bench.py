@@ -315,19 +315,21 @@ def main():
     runner.close()
     if a.configs and a.workload == "full_bf16_packs2048" and not a.merged and a.output == "pooled":
         line["configs"] = {}
-        for name, steps in SECONDARY:
-            log(f"config {name}")
-            r = Runner(torch, ti, B, Model, name, a.streams, host_threads=a.host_threads)
+        for key, name, steps, streams, split_k in SECONDARY:
+            log(f"config {key}")
+            r = Runner(torch, ti, B, Model, name, streams or a.streams, split_k=split_k, host_threads=a.host_threads)
             r.run_steps(2)
             torch.cuda.synchronize()
             sec = r.timed(steps)
             bd = r.breakdown()
             dom = max((g for g in KERNEL_GROUPS if any(bd.get(c, {}).get("launches") for c in KERNEL_GROUPS[g])),
                       key=lambda g: sum(bd.get(c, {}).get("ms", 0.0) for c in KERNEL_GROUPS[g]))
-            line["configs"][name] = {
+            line["configs"][key] = {
                 "tokens_per_s": round(r.tokens_per_step * steps / sec, 1), "ms_per_step": round(sec * 1e3 / steps, 3),
-                "steps": steps, "warmup": 2, "streams": r.S, "calls_per_step": len(r.packs), "tokens_per_step": r.tokens_per_step,
+                "steps": steps, "warmup": 2, "streams": r.S, "split_k": split_k, "calls_per_step": len(r.packs),
+                "tokens_per_step": r.tokens_per_step,
                 "dtype": DTYPE[r.cfg.precision], "dominant_kernel": dom, "dominant_frac_of_peak": group_frac(bd, dom),
+                "residual_frac_of_peak": group_frac(bd, "k_gemm residual (Wo + Wo2)"),
                 "kernels": public(bd)}
             r.close()
             torch.cuda.empty_cache()
@@ -337,9 +339,15 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-# other workloads measured in the default run: (name, timed steps)
-SECONDARY = [("full_fp32_957", 30), ("full_bf16_4x4096", 10), ("full_int8_packs2048", 10),
-             ("full_int4_packs2048", 10)]
+# other lines measured in the default run: (key, workload, timed steps,
+# streams (None: --streams), TTE_FLAG_SPLIT_K).  The last is the headline
+# workload as a single caller would run it: one stream, the down-projection
+# split over K so that a lone pack fills the CUs (lower latency per pack).
+SECONDARY = [("full_fp32_957", "full_fp32_957", 30, None, False),
+             ("full_bf16_4x4096", "full_bf16_4x4096", 10, None, False),
+             ("full_int8_packs2048", "full_int8_packs2048", 10, None, False),
+             ("full_int4_packs2048", "full_int4_packs2048", 10, None, False),
+             ("full_bf16_packs2048_one_stream_split_k", "full_bf16_packs2048", 5, 1, True)]
 
 
 def public(bd):
@@ -360,6 +368,20 @@ def group_frac(bd, group):
     ms = sum(bd[c]["ms"] for c in present)
     unit_scale = 1e12 if "TFLOP/s" in bd[present[0]] else 1e9
     return round(work / (ms / 1e3) / unit_scale / bd[present[0]]["_peak"], 4) if ms else None
+
+
+_STREAMS = []
+
+
+def shared_streams(torch, dev, n):
+    """The first n of one list of streams that every Runner of the process
+    shares.  HIP maps streams onto its hardware queues in creation order
+    and reuses them round-robin, so fresh streams for each workload would
+    land on queues that other (idle) streams already hold; reusing the
+    same streams keeps every workload's packs on their own queues."""
+    while len(_STREAMS) < n:
+        _STREAMS.append(torch.cuda.Stream(device=dev))
+    return _STREAMS[:n]
 
 
 class Runner:
@@ -394,7 +416,7 @@ class Runner:
         self.models = [model] + [Model(cfg, None, max_tokens=max_tokens, max_text_len=max_len, max_texts=max_texts,
                                        device="cuda:0", shared_from=model, split_k=split_k, graph=graph)
                                  for _ in range(S - 1)]
-        self.streams = [torch.cuda.Stream(device=dev) for _ in range(S)]
+        self.streams = shared_streams(torch, dev, S)
         self.ids = [torch.from_numpy(p.ids).to(dev) for p in packs]
         self.outs = [torch.empty((p.n_tokens if per_token else p.n_texts, cfg.hidden), dtype=torch.float32,
                                  device=dev) for p in packs]
