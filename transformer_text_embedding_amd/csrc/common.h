@@ -65,6 +65,23 @@ __device__ __forceinline__ float wave_max(float v) {
 }
 #undef TTE_DPP
 
+// The largest b with a[b] <= v in the strictly increasing a[0..n] (a[0] <=
+// v), returned to every lane: the whole wave reads the n + 1 entries 64 at
+// a time and counts those <= v, so a pack's texts cost one load round
+// instead of a binary search's chain of dependent loads.  Every lane of the
+// wave must call it, with the same v.
+__device__ __forceinline__ int wave_find(const int* __restrict__ a, int n, int v) {
+  const int lane = (int)__lane_id();
+  int count = 0;
+  for (int base = 0; base <= n; base += WAVE) {
+    const int i = base + lane;
+    const uint64_t m = __ballot(i <= n && a[i] <= v);
+    count += __popcll(m);
+    if (m != ~0ull) break;
+  }
+  return count - 1;
+}
+
 // 7-bit row code: clamp(rint(x * inv), -63, 63) with ties to even.
 __device__ __forceinline__ int quant7(float x, float inv) {
   float q = __builtin_rintf(x * inv);

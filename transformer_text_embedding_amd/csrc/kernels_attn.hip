@@ -83,12 +83,8 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
   int i0, q_end;
   if (qunit) {
     const int u = blockIdx.x;
-    if (u >= qunit[n_texts]) return;
-    int lo = 0, hi = n_texts;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (qunit[mid] <= u) lo = mid; else hi = mid;
-    }
+    const int lo = wave_find(qunit, n_texts, u);  // the unit's text
+    if (lo >= n_texts) return;                     // u is past the last unit
     i0 = off[lo] + BQ * (u - qunit[lo]);
     q_end = min(i0 + BQ, off[lo + 1]);
   } else {

@@ -139,6 +139,7 @@ __global__ __launch_bounds__(256) void k_embed_ln(const int32_t* __restrict__ id
   if (io) ids = io->ids;
   int id = ids[t];
   id = id < 0 ? 0 : (id >= vocab ? vocab - 1 : id);
+  const int b = wave_find(off, n_texts, t);  // the token's text (off strictly increasing, off[0] = 0)
   float v[EPL];
   if constexpr (PREC == P_F32) {
     load_f32_row<EPL>(reinterpret_cast<const float*>(table) + (size_t)id * H, lane, v);
@@ -161,15 +162,7 @@ __global__ __launch_bounds__(256) void k_embed_ln(const int32_t* __restrict__ id
   }
   layernorm_regs<EPL>(v, gamma, lane, eps);
   store_f32_row<EPL>(x + (size_t)t * H, lane, v);
-  if (lane == 0) {
-    // largest b with off[b] <= t (off is strictly increasing, off[0] = 0)
-    int lo = 0, hi = n_texts;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (off[mid] <= t) lo = mid; else hi = mid;
-    }
-    seg[t] = Seg{off[lo], off[lo + 1]};
-  }
+  if (lane == 0) seg[t] = Seg{off[b], off[b + 1]};
 }
 
 // --------------------------------------------------------------------------
@@ -261,22 +254,28 @@ __global__ __launch_bounds__(256) void k_pool_partial(const float* __restrict__ 
   __shared__ float red[4][H];
   const int u = blockIdx.x;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int lo = 0, hi = n_texts;  // text b with unit_start[b] <= u < unit_start[b+1]
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (unit_start[mid] <= u) lo = mid; else hi = mid;
-  }
+  const int lo = wave_find(unit_start, n_texts, u);  // text b with unit_start[b] <= u < unit_start[b+1]
   const int r0 = off[lo] + (u - unit_start[lo]) * POOL_ROWS;
   const int r1 = min(r0 + POOL_ROWS, off[lo + 1]);
   float acc[EPL];
 #pragma unroll
   for (int i = 0; i < EPL; ++i) acc[i] = 0.f;
-  for (int r = r0 + w; r < r1; r += 4) {
-    float v[EPL];
-    load_f32_row<EPL>(x + (size_t)r * H, lane, v);
-    layernorm_regs<EPL>(v, gamma, lane, eps);
+  // a wave's rows r0 + w, r0 + w + 4, ...: RB rows' loads in flight at a
+  // time, then normalised and added in row order
+  constexpr int RB = EPL <= 12 ? 8 : (EPL <= 24 ? 4 : (EPL <= 48 ? 2 : 1));
+  for (int rb = r0 + w; rb < r1; rb += 4 * RB) {
+    float v[RB][EPL];
 #pragma unroll
-    for (int i = 0; i < EPL; ++i) acc[i] += v[i];
+    for (int k = 0; k < RB; ++k)
+      if (rb + 4 * k < r1) load_f32_row<EPL>(x + (size_t)(rb + 4 * k) * H, lane, v[k]);
+#pragma unroll
+    for (int k = 0; k < RB; ++k) {
+      if (rb + 4 * k < r1) {  // wave-uniform
+        layernorm_regs<EPL>(v[k], gamma, lane, eps);
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) acc[i] += v[k][i];
+      }
+    }
   }
 #pragma unroll
   for (int c = 0; c < RS::CH; ++c)
@@ -305,8 +304,18 @@ __global__ __launch_bounds__(256) void k_pool_finish(const float* __restrict__ p
   for (int i = 0; i < PER; ++i) {
     const int j = threadIdx.x + 256 * i;
     float s = 0.f;
-    if (j < H)
-      for (int u = u0; u < u1; ++u) s += partial[(size_t)u * H + j];
+    if (j < H) {
+      // 8 units' loads in flight at a time, then added in unit order (the
+      // same sum as one unit at a time, without a load latency per unit)
+      for (int u = u0; u < u1; u += 8) {
+        float t[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t[k] = u + k < u1 ? partial[(size_t)(u + k) * H + j] : 0.f;
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+          if (u + k < u1) s += t[k];
+      }
+    }
     e[i] = s * inv_n;
     ss += (j < H) ? e[i] * e[i] : 0.f;
   }
