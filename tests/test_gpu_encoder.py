@@ -204,6 +204,26 @@ def test_edge_cases(tiny_models):
     _gate(got, ref, "fp32")
 
 
+def test_many_texts_per_pack():
+    """Packs of 130 and 200 short texts: every per-token and per-unit
+    lookup of a token's or a unit's text reads the offsets in several
+    64-entry rounds (global attention's query units, the pool's row units,
+    the embedding's text bounds)."""
+    cfg, w = _tiny("fp32")
+    m = Model(cfg, w, max_tokens=2048, max_text_len=1024, max_texts=256)
+    try:
+        rng = np.random.default_rng(9)
+        for n in (130, 200):
+            lengths = [int(x) for x in rng.integers(1, 13, size=n)]
+            lengths[n // 2] = 90  # one text longer than a 64-query unit
+            pack = ti.random_pack(rng, lengths, cfg.vocab)
+            got = host(m.embed_pack(dev(pack.ids), pack.offsets))
+            ref = oracle.encode(cfg.as_dict(), w, pack.ids, pack.offsets)
+            _gate(got, ref, "fp32")
+    finally:
+        m.close()
+
+
 def test_embed_helper_packs_whole_texts(tiny_models):
     cfg, w, m = tiny_models["fp32"]
     rng = np.random.default_rng(4)
