@@ -222,7 +222,8 @@ def main():
                          "as concurrent request handlers would)")
     ap.add_argument("--graph", action="store_true",
                     help="TTE_FLAG_GRAPH: replay each pack's captured HIP graph (needs --warmup >= 2)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=3000)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=7000,
+                    help="the CPU oracle times the first packs covering this many tokens (~15 s on 16 host threads)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kernel-events", action="store_true",
                     help="time the steps without the per-launch events of the dominant kernel")
