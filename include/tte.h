@@ -28,6 +28,19 @@
  *     has reached the enqueued work.
  *   - Matrices are row-major.  Activations are token-major [T, H].  Weights
  *     are [out, in], so every projection is Y = X * W^T.
+ *
+ * Diagnostics, read from the environment once per process (set to any value
+ * but "0"):
+ *   - TTE_LOG: one stderr line per tte_create, per pass of tte_embed /
+ *     tte_embed_tokens / tte_embed_trace and per error, prefixed "[tte]".
+ *   - TTE_DEBUG: host-side checks around every pass of those three entry
+ *     points, each of which waits for the stream (for finding faults, not
+ *     for timing): the token ids are read back and must lie in [0, vocab)
+ *     (TTE_E_INVALID before anything is enqueued; without TTE_DEBUG they
+ *     are clamped on the device); a 256-byte guard after every workspace
+ *     region (tte_workspace_size grows accordingly) must keep its fill
+ *     after the pass; the outputs must be finite, pooled vectors of unit
+ *     length (TTE_E_DEVICE otherwise).  TTE_FLAG_GRAPH is ignored.
  */
 #ifndef TTE_H
 #define TTE_H

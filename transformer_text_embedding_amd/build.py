@@ -81,8 +81,67 @@ def build(jobs: int = 4, verbose: bool = False) -> str:
     return LIB
 
 
+# CPU tier: the engine's host code (argument checks, workspace layout, pack
+# validation, staging) with AddressSanitizer and UndefinedBehaviorSanitizer.
+# Every -fsanitize= is a host-only flag: the device code is compiled as in
+# the library, and nothing here runs on a GPU.
+SANITIZE_DIR = os.path.join(BUILD, "host_sanitize")
+SANITIZE_LIB = os.path.join(SANITIZE_DIR, "libtte_host_sanitized.so")
+SANITIZE_DRIVER = os.path.join(SANITIZE_DIR, "host_sanitizer_driver")
+DRIVER_SRC = os.path.join(ROOT, "tests", "host_sanitizer_driver.cpp")
+HOST_SANITIZE = [
+    "-Xarch_host", "-fsanitize=address",
+    "-Xarch_host", "-fsanitize=undefined",
+    "-Xarch_host", "-fno-sanitize-recover=undefined",
+    "-Xarch_host", "-fno-omit-frame-pointer",
+]
+
+
+def host_clangxx() -> str:
+    for c in ("/opt/rocm/llvm/bin/clang++", "/opt/rocm/lib/llvm/bin/clang++", shutil.which("clang++")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("clang++ not found")
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libtte_host_sanitized.so (tte.hip with the host sanitizers, linked
+    with the regular kernel objects) and the driver that exercises its
+    GPU-free paths; returns the driver's path."""
+    os.makedirs(SANITIZE_DIR, exist_ok=True)
+    kernel_objs = []
+    for src in SOURCES:
+        if src == "tte.hip":
+            continue
+        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        kernel_objs.append(obj if os.path.exists(obj) else _compile(src))
+    obj = os.path.join(SANITIZE_DIR, "tte.o")
+    cmd = [hipcc(), *HIPCC_FLAGS, *HOST_SANITIZE, "-c", os.path.join(CSRC, "tte.hip"), "-o", obj]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"hipcc failed on tte.hip (host sanitizers):\n{r.stdout}{r.stderr}")
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", SANITIZE_LIB, obj, *kernel_objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed (host sanitizers):\n{r.stdout}{r.stderr}")
+    # the driver is plain C++ (no HIP source), built by the host compiler
+    cmd = [host_clangxx(), "-O1", "-g", "-std=c++17", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", "-I", INCLUDE, DRIVER_SRC, "-o", SANITIZE_DRIVER,
+           "-L", SANITIZE_DIR, "-ltte_host_sanitized", f"-Wl,-rpath,{SANITIZE_DIR}"]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"driver build failed:\n{r.stdout}{r.stderr}")
+    if verbose:
+        print(f"built {SANITIZE_DRIVER}")
+    return SANITIZE_DRIVER
+
+
 if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--jobs", type=int, default=4)
+    ap.add_argument("--host-sanitize", action="store_true",
+                    help="also build the host-sanitizer library and driver (CPU tier)")
     a = ap.parse_args()
     build(a.jobs, verbose=True)
+    if a.host_sanitize:
+        build_host_sanitized(verbose=True)

@@ -11,7 +11,9 @@
 #include <hip/hip_runtime.h>
 
 #include <cmath>
+#include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -26,10 +28,46 @@ namespace {
 
 thread_local std::string g_err;
 
+// Diagnostics switched on from the environment (read once per process):
+// TTE_LOG=1 writes one stderr line per model creation, per pass and per
+// error; TTE_DEBUG=1 adds host-side checks around every pass, each of which
+// waits for the stream (slow; for finding faults, not for timing): token
+// ids in [0, vocab) (the normal path clamps them on the device), guard
+// words after every workspace region intact, and the outputs finite (pooled
+// vectors of unit length).
+bool env_on(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] && std::strcmp(v, "0") != 0;
+}
+bool log_on() {
+  static const bool on = env_on("TTE_LOG");
+  return on;
+}
+bool debug_on() {
+  static const bool on = env_on("TTE_DEBUG");
+  return on;
+}
+
+__attribute__((format(printf, 1, 2))) void log_line(const char* fmt, ...) {
+  if (!log_on()) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[tte] %s\n", buf);
+}
+
 tte_status fail(tte_status s, const std::string& msg) {
   g_err = msg;
+  log_line("error %d: %s", (int)s, msg.c_str());
   return s;
 }
+
+// TTE_DEBUG: bytes of the guard after each workspace region, and its fill
+constexpr size_t GUARD_BYTES = 256;
+constexpr unsigned char GUARD_FILL = 0xA5;
+constexpr int MAX_GUARDS = 16;
 
 size_t al(size_t v) { return (v + 255) & ~size_t(255); }
 
@@ -40,6 +78,8 @@ struct Layout {
   size_t x, xa, ascale, qkv, vt, o, y, kpart, seg, off, partial, cosg, sing, cosl, sinl, total;
   int max_units;
   int vt_stride;
+  size_t guard[MAX_GUARDS];  // TTE_DEBUG: a guard after every region
+  int n_guards;
 };
 
 int act_bytes(int prec) { return prec == TTE_BF16 ? 2 : 4; }
@@ -50,9 +90,14 @@ Layout layout_of(const tte_config& c) {
   const size_t ab = (size_t)act_bytes(c.precision);
   L.max_units = c.max_tokens / POOL_ROWS + c.max_texts + 1;
   size_t p = 0;
+  const bool guards = debug_on();
   auto take = [&](size_t bytes) {
     const size_t at = p;
     p += al(bytes);
+    if (guards && L.n_guards < MAX_GUARDS) {
+      L.guard[L.n_guards++] = p;
+      p += GUARD_BYTES;
+    }
     return at;
   };
   L.x = take(T * H * 4);
@@ -444,6 +489,59 @@ tte_model::GraphEntry* graph_entry(tte_model* m, int kind, int T, int B, int uni
   return &m->graphs.back();
 }
 
+// TTE_DEBUG, before a pass: the pack's token ids, read back (the stream
+// waits), must lie in [0, vocab).
+tte_status debug_check_ids(const tte_model* m, const int32_t* d_ids, int32_t T, hipStream_t s) {
+  std::vector<int32_t> ids((size_t)T);
+  tte_status st = hip_check(hipMemcpyAsync(ids.data(), d_ids, sizeof(int32_t) * (size_t)T, hipMemcpyDeviceToHost, s),
+                            "hipMemcpyAsync(ids)");
+  if (st == TTE_OK) st = hip_check(hipStreamSynchronize(s), "hipStreamSynchronize");
+  if (st != TTE_OK) return st;
+  for (int32_t t = 0; t < T; ++t)
+    if (ids[t] < 0 || ids[t] >= m->cfg.vocab)
+      return fail(TTE_E_INVALID, "TTE_DEBUG: token id " + std::to_string(ids[t]) + " at index " + std::to_string(t) +
+                                     " is outside [0, vocab)");
+  return TTE_OK;
+}
+
+// TTE_DEBUG, after a pass: the stream's work completed without error, every
+// workspace guard still holds its fill, and the outputs are finite (pooled
+// vectors of unit length, unless all zero).
+tte_status debug_check_after(const tte_model* m, hipStream_t s, int32_t T, int32_t B, const float* d_out,
+                             const float* d_tok) {
+  tte_status st = hip_check(hipStreamSynchronize(s), "TTE_DEBUG: the pass");
+  if (st != TTE_OK) return st;
+  unsigned char g[GUARD_BYTES];
+  for (int i = 0; i < m->L.n_guards; ++i) {
+    st = hip_check(hipMemcpy(g, m->ws + m->L.guard[i], GUARD_BYTES, hipMemcpyDeviceToHost), "hipMemcpy(guard)");
+    if (st != TTE_OK) return st;
+    for (size_t k = 0; k < GUARD_BYTES; ++k)
+      if (g[k] != GUARD_FILL)
+        return fail(TTE_E_DEVICE, "TTE_DEBUG: workspace guard " + std::to_string(i) + " overwritten at byte " +
+                                      std::to_string(k));
+  }
+  const int H = m->cfg.hidden;
+  const bool pooled = d_out != nullptr;
+  const float* src = pooled ? d_out : d_tok;
+  if (!src) return TTE_OK;
+  const size_t rows = (size_t)(pooled ? B : T);
+  std::vector<float> v(rows * (size_t)H);
+  st = hip_check(hipMemcpy(v.data(), src, v.size() * 4, hipMemcpyDeviceToHost), "hipMemcpy(out)");
+  if (st != TTE_OK) return st;
+  for (size_t r = 0; r < rows; ++r) {
+    double ss = 0.0;
+    for (int j = 0; j < H; ++j) {
+      const float x = v[r * H + j];
+      if (!std::isfinite(x))
+        return fail(TTE_E_DEVICE, "TTE_DEBUG: output row " + std::to_string(r) + " is not finite");
+      ss += (double)x * x;
+    }
+    if (pooled && ss > 0.0 && std::fabs(std::sqrt(ss) - 1.0) > 1e-3)
+      return fail(TTE_E_DEVICE, "TTE_DEBUG: output row " + std::to_string(r) + " is not of unit length");
+  }
+  return TTE_OK;
+}
+
 // Validates and uploads a pack, then runs the pass: eagerly, or with
 // TTE_FLAG_GRAPH from the graph of the pack's shape (captured at the
 // shape's second call).
@@ -466,7 +564,12 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
   st = hip_check(hipSetDevice(m->device), "hipSetDevice");
   if (st != TTE_OK) return st;
   (void)hipGetLastError();
-  const bool graph = (c.flags & TTE_FLAG_GRAPH) && !d_states && s != nullptr && !m->prof_on;
+  const bool debug = debug_on();
+  const bool graph = (c.flags & TTE_FLAG_GRAPH) && !d_states && s != nullptr && !m->prof_on && !debug;
+  if (debug) {
+    st = debug_check_ids(m, d_ids, T, s);
+    if (st != TTE_OK) return st;
+  }
   int n_units = 0;
   st = upload_pack(m, h_off, B, &n_units, s, graph ? d_ids : nullptr, graph ? (d_tok ? d_tok : d_out) : nullptr);
   if (st != TTE_OK) return st;
@@ -498,13 +601,18 @@ tte_status run_pass(tte_model* m, const int32_t* d_ids, int32_t T, const int32_t
     }
     if (e->exec) {
       ++m->graph_replays;
+      log_line("pass: %d tokens, %d texts, %d pool units, graph replay, stream %p", T, B, n_units, (void*)s);
       st = hip_check(hipGraphLaunch(e->exec, s), "hipGraphLaunch");
       if (st != TTE_OK) return st;
       return hip_check(hipEventRecord(e->done, s), "hipEventRecord(graph replay)");
     }
   }
+  log_line("pass: %d tokens, %d texts, %d pool units, %d layers%s, %s output, stream %p", T, B, n_units, n_run,
+           d_states ? " (states dumped)" : "", d_tok ? "per-token" : "pooled", (void*)s);
   enqueue_pass(m, d_ids, io, T, B, n_units, d_out, d_states, n_run, d_tok, s);
-  return hip_check(hipGetLastError(), "kernel launch");
+  st = hip_check(hipGetLastError(), "kernel launch");
+  if (st == TTE_OK && debug) st = debug_check_after(m, s, T, B, n_run == c.n_layers ? d_out : nullptr, n_run == c.n_layers ? d_tok : nullptr);
+  return st;
 }
 
 // --------------------------------------------------------------------------
@@ -668,6 +776,8 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   // key tiles that run past the pack: keep them finite
   if (st == TTE_OK)
     st = hip_check(hipMemset(m->vt, 0, (size_t)c.hidden * L.vt_stride * act_bytes(c.precision)), "hipMemset(vt)");
+  for (int i = 0; i < L.n_guards && st == TTE_OK; ++i)
+    st = hip_check(hipMemset(b + L.guard[i], GUARD_FILL, GUARD_BYTES), "hipMemset(guard)");
   if (st == TTE_OK)
     st = hip_check(hipHostMalloc((void**)&m->h_stage, sizeof(int) * stage_ints(c) * STAGE_SLOTS, hipHostMallocDefault),
                    "hipHostMalloc");
@@ -681,6 +791,10 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
     return st;
   }
   *out = m;
+  log_line("create: precision %d, %d layers, hidden %d, intermediate %d, max_tokens %d, max_texts %d, "
+           "max_text_len %d, flags %d, workspace %zu bytes%s, device %d",
+           c.precision, c.n_layers, c.hidden, c.intermediate, c.max_tokens, c.max_texts, c.max_text_len, c.flags,
+           (size_t)L.total, L.n_guards ? " (with guards)" : "", m->device);
   return TTE_OK;
 }
 
