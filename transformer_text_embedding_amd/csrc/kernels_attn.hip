@@ -71,10 +71,23 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
   constexpr int BQ = 4 * QPW;   // queries per block
   extern __shared__ __attribute__((aligned(1024))) uint8_t smem[];
   const int H = nh * 64, ld = 3 * H;
-  const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, g = lane >> 4, li = lane & 15;
+  // XCD-aware order: block b of the launch runs on XCD b mod 8, so XCD x
+  // takes a contiguous run of the (head, query block) pairs in head-major
+  // order; a head's keys and values are then fetched into one or two XCDs'
+  // L2 instead of all eight, and neighbouring query blocks (whose local
+  // windows share key tiles) meet in the same L2.
+  int h, qblk;
+  {
+    const int nx = gridDim.x, total = nx * gridDim.y;
+    const int b = blockIdx.y * nx + blockIdx.x;
+    const int xcd = b & 7, local = b >> 3, per = total >> 3, extra = total & 7;
+    const int wi = xcd * per + min(xcd, extra) + local;
+    h = wi / nx;
+    qblk = wi - h * nx;
+  }
 
-  // The block's queries [i0, q_end): with qunit, unit blockIdx.x of the
+  // The block's queries [i0, q_end): with qunit, unit qblk of the
   // per-text units of BQ queries (text b owns units qunit[b] ..
   // qunit[b+1] - 1), so a block never spans two texts and walks only its
   // own text's keys; the grid covers an upper bound of the unit count and
@@ -82,13 +95,13 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
   // the pack.
   int i0, q_end;
   if (qunit) {
-    const int u = blockIdx.x;
+    const int u = qblk;
     const int lo = wave_find(qunit, n_texts, u);  // the unit's text
     if (lo >= n_texts) return;                     // u is past the last unit
     i0 = off[lo] + BQ * (u - qunit[lo]);
     q_end = min(i0 + BQ, off[lo + 1]);
   } else {
-    i0 = blockIdx.x * BQ;
+    i0 = qblk * BQ;
     q_end = min(i0 + BQ, T);
   }
 
