@@ -251,6 +251,31 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
   if constexpr (PREC == P_I8 || PREC == P_I4)
     s_src = w_scale + (size_t)w_row<EPI, BN, WGN>(wid * 32 + (lane & 31), nb, N) * (K / 32) + split * (k_part / 32);
 
+  // bf16 residual products in tiles of at most 8 MFMA tiles per wave (32
+  // more registers; larger wave tiles would spill): the x values this lane
+  // adds in the epilogue (its WN 16-byte chunks of each of its WM 16-row
+  // slabs, in the epilogue's lane order) are loaded before the K loop, so
+  // their latency overlaps the loop instead of following it.  No block
+  // writes another block's part of x, and the loop's waits for its own
+  // (younger) tile loads also cover these.
+  constexpr bool XPRE = EPI == E_RESID && PREC == P_BF16 && WM * WN <= 8;
+  f32x4 xpre[XPRE ? WM : 1][XPRE ? WN : 1];
+  if constexpr (XPRE) {
+    constexpr int XCPR = 4 * WN;  // 16-byte chunks of a wave's 16 WN fp32 columns
+    const int n_wave = nb * BN + wn * 16 * WN;
+#pragma unroll
+    for (int mt = 0; mt < WM; ++mt) {
+      const int m_slab = m0 + wm * 16 * WM + mt * 16;
+#pragma unroll
+      for (int i = 0; i < WN; ++i) {
+        const int c = lane + 64 * i, row = c / XCPR, cc = c % XCPR, m = m_slab + row;
+        xpre[mt][i] = m < M ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(C) + (size_t)m * N + n_wave + 4 * cc)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    asm volatile("" ::: "memory");  // issued here, ahead of the first K tiles
+  }
+
   f32x4 acc[WM][WN];
 #pragma unroll
   for (int a = 0; a < WM; ++a)
@@ -642,13 +667,16 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
       // would otherwise wait for each chunk's load behind the previous store)
       constexpr int NI = 16 * CPR / 64;
       static_assert(NI * 64 == 16 * CPR, "whole chunks per lane");
+      static_assert(!XPRE || NI == WN, "the prefetched chunks are the epilogue's");
       f32x4 ov[NI], dv[NI];
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int c = lane + 64 * i, row = c / CPR, cc = c % CPR, m = m_slab + row;
         dv[i] = *reinterpret_cast<const f32x4*>(slab + row * RB + cc * 16);
-        ov[i] = m < M ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(C) + (size_t)m * N + n_wave + 4 * cc)
-                      : f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (XPRE) ov[i] = xpre[mt][i];
+        else
+          ov[i] = m < M ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(C) + (size_t)m * N + n_wave + 4 * cc)
+                        : f32x4{0.f, 0.f, 0.f, 0.f};
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
