@@ -155,28 +155,64 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
     }
   }
 
-  // ---- load plan: instruction j of wave w covers tile rows
-  // ROWS_PER_Q * (w * QW + j) + lane / (ROWB / 16); rows 0..63 are K rows,
-  // rows 64..127 are V^T rows (dims) ----
+  // ---- load plan: instruction j of wave w (q = w * QW + j) fills tile
+  // rows ROWS_PER_Q * q .. + ROWS_PER_Q - 1: K rows while ROWS_PER_Q * q <
+  // 64 (a wave-uniform test), V^T rows (dims) after.  Each source is a
+  // wave-uniform base that advances by one tile of keys per tile plus a
+  // per-lane 32-bit offset fixed before the loop, so a tile's loads take no
+  // vector address arithmetic; only a K tile running past the pack's last
+  // token clamps its rows (V^T has 64 columns of slack). ----
   constexpr int CPR = C::ROWB / 16;  // 16-byte chunks per row
   const int j_first = kstart & ~(C::ALIGN - 1);
   const int n_tiles = (kend - j_first + AKT - 1) / AKT;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int lrow = lane / CPR, lslot = lane % CPR;
+  const uint32_t k_row_bytes = (uint32_t)ld * C::ES;
+  const uint8_t* k_base = reinterpret_cast<const uint8_t*>(qk) + (size_t)(H + h * 64) * C::ES;
+  const uint8_t* v_base = reinterpret_cast<const uint8_t*>(vt) + ((size_t)(h * 64) * vt_stride + j_first) * C::ES;
+  // the 32-bit offsets cover every source byte of the pack (else the
+  // tiles take the 64-bit form below)
+  const bool off32 = (size_t)(T + AKT) * k_row_bytes < ((size_t)1 << 32) &&
+                     (size_t)H * (size_t)vt_stride * C::ES < ((size_t)1 << 32);
+  uint32_t src_off[C::QW];
+#pragma unroll
+  for (int j = 0; j < C::QW; ++j) {
+    const int q = wu * C::QW + j;
+    const int row = C::ROWS_PER_Q * q + lrow;
+    const uint32_t chunk = (uint32_t)((lslot ^ (row & 7)) * 16);
+    src_off[j] = C::ROWS_PER_Q * q < 64 ? (uint32_t)(j_first + row) * k_row_bytes + chunk
+                                        : (uint32_t)(row - 64) * (uint32_t)vt_stride * C::ES + chunk;
+  }
   auto issue = [&](int t) {
     uint8_t* stage = smem + (t % C::STAGES) * C::TILE;
-    const int j0 = j_first + t * AKT;
+    // every K row of the tile is a token of the pack
+    if (off32 && j_first + (t + 1) * AKT <= T) {
+      // the wave's loads are all K rows or all V^T rows
+      static_assert(64 % (C::QW * C::ROWS_PER_Q) == 0, "a wave's rows never straddle K and V^T");
+      if (C::ROWS_PER_Q * wu * C::QW < 64) {
+        const uint8_t* base = k_base + (size_t)t * AKT * k_row_bytes;
 #pragma unroll
-    for (int j = 0; j < C::QW; ++j) {
-      const int q = w * C::QW + j;
-      const int row = C::ROWS_PER_Q * q + lane / CPR;
-      const int chunk = (lane % CPR) ^ (row & 7);
-      const uint8_t* src;
-      if (row < 64) {
-        const int kr = min(j0 + row, T - 1);
-        src = reinterpret_cast<const uint8_t*>(qk) + ((size_t)kr * ld + H + h * 64) * C::ES + chunk * 16;
+        for (int j = 0; j < C::QW; ++j) dma16(base + src_off[j], stage + (wu * C::QW + j) * 1024);
       } else {
-        src = reinterpret_cast<const uint8_t*>(vt) + ((size_t)(h * 64 + row - 64) * vt_stride + j0) * C::ES + chunk * 16;
+        const uint8_t* base = v_base + (size_t)t * AKT * C::ES;
+#pragma unroll
+        for (int j = 0; j < C::QW; ++j) dma16(base + src_off[j], stage + (wu * C::QW + j) * 1024);
       }
-      dma16(src, stage + q * 1024);
+    } else {
+#pragma unroll
+      for (int j = 0; j < C::QW; ++j) {
+        const int q = wu * C::QW + j;
+        const int row = C::ROWS_PER_Q * q + lrow;
+        const size_t chunk = (size_t)((lslot ^ (row & 7)) * 16);
+        const uint8_t* src;
+        if (C::ROWS_PER_Q * q < 64) {
+          const int kr = min(j_first + t * AKT + row, T - 1);
+          src = k_base + (size_t)kr * k_row_bytes + chunk;
+        } else {
+          src = v_base + ((size_t)(row - 64) * vt_stride + (size_t)t * AKT) * C::ES + chunk;
+        }
+        dma16(src, stage + q * 1024);
+      }
     }
   };
 
