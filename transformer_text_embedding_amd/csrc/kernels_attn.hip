@@ -46,6 +46,24 @@ namespace {
 constexpr int AKT = 64;  // keys per tile
 constexpr float NEG_INF = -__builtin_huge_valf();
 
+// Max / sum over lanes l, l ^ 16, l ^ 32, l ^ 48 (the four 16-lane rows'
+// copies of one query column), returned to all four: the gfx950 row-swap
+// moves pair rows (0,1), (2,3) and then (01, 23) in registers, with no LDS
+// crossbar trip.  Pairs combine in a fixed order (row 0's operand first),
+// so every lane gets the same, deterministic value.
+__device__ __forceinline__ float rows_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+__device__ __forceinline__ float rows_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
 template <int PREC, int STAGES_ = 2>
 struct AttnCfg {
   static constexpr int ES = PREC == P_F32 ? 4 : 2;
@@ -279,28 +297,23 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
     float sv[NQ][16];
 #pragma unroll
     for (int qt = 0; qt < NQ; ++qt) {
-      float mloc = NEG_INF;
       const int kb = j0 + 4 * g - k_lo[qt];  // key offset of element (0, 0) from k_lo
-      if (__all((unsigned)kb < k_span[qt] && (unsigned)(kb + 51) < k_span[qt])) {
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sv[qt][mt * 4 + r] = sacc[qt][mt][r];
+      if (!__all((unsigned)kb < k_span[qt] && (unsigned)(kb + 51) < k_span[qt])) {
+        // some key of the tile is outside some lane's range: mask in place
 #pragma unroll
         for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            sv[qt][mt * 4 + r] = sacc[qt][mt][r];
-            mloc = fmaxf(mloc, sv[qt][mt * 4 + r]);
-          }
-      } else {
-#pragma unroll
-        for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const bool ok = (unsigned)(kb + 16 * mt + r) < k_span[qt];
-            sv[qt][mt * 4 + r] = ok ? sacc[qt][mt][r] : NEG_INF;
-            mloc = fmaxf(mloc, sv[qt][mt * 4 + r]);
-          }
+          for (int r = 0; r < 4; ++r)
+            if (!((unsigned)(kb + 16 * mt + r) < k_span[qt])) sv[qt][mt * 4 + r] = NEG_INF;
       }
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 16, 64));
-      mloc = fmaxf(mloc, __shfl_xor(mloc, 32, 64));
+      float mloc = NEG_INF;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sv[qt][i]);
+      mloc = rows_max(mloc);
       const float m_new = fmaxf(m_run[qt], mloc);
       const float m_use = m_new == NEG_INF ? 0.f : m_new;
       // the output and sum are rescaled only when some lane's running max
@@ -321,9 +334,7 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
         float psum = 0.f;
 #pragma unroll
         for (int i = 0; i < 16; ++i) psum += sv[qt][i];
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        l_run[qt] += psum;
+        l_run[qt] += rows_sum(psum);
       }
     }
 
