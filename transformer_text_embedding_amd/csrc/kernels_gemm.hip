@@ -592,9 +592,11 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
           if constexpr (OUT == O_BF16) {
             uint16_t* vp = reinterpret_cast<uint16_t*>(qo.vt) + at;
             if (mr + 3 < M) {
-              const u16x4 t = {f32_to_bf16(acc[mt][nt][0] * rs[0]), f32_to_bf16(acc[mt][nt][1] * rs[1]),
-                               f32_to_bf16(acc[mt][nt][2] * rs[2]), f32_to_bf16(acc[mt][nt][3] * rs[3])};
-              *reinterpret_cast<u16x4*>(vp) = t;
+              // the hardware pack-convert: round to nearest even, as
+              // f32_to_bf16 for the finite values here
+              const uint32_t lo = pack_bf16x2(acc[mt][nt][0] * rs[0], acc[mt][nt][1] * rs[1]);
+              const uint32_t hi = pack_bf16x2(acc[mt][nt][2] * rs[2], acc[mt][nt][3] * rs[3]);
+              *reinterpret_cast<uint2*>(vp) = uint2{lo, hi};
             } else {
 #pragma unroll
               for (int r = 0; r < 4; ++r)
