@@ -62,8 +62,9 @@ typedef enum {
 
 typedef enum {
   TTE_FP32 = 0, /* fp32 weights and activations, fp32 matrix cores */
-  TTE_BF16 = 1, /* bf16 weights and matmul/attention operands, fp32 accumulate,
-                   fp32 residual stream, norms and softmax statistics */
+  TTE_BF16 = 1, /* bf16 weights, matmul/attention operands and residual
+                   stream (each update added in fp32, rounded once); fp32
+                   accumulate, norms and softmax statistics */
   TTE_INT8 = 2, /* int8 weight blocks of 32 inputs with fp32 scales; every
                    weight matmul input rounded per row to 7 bits (|q| <= 63)
                    with an fp32 row scale; int8 matrix cores, int32 sums per
@@ -213,7 +214,8 @@ tte_status tte_similarity(const float* d_emb, int32_t n, int32_t dim, float* d_s
 
 /* Like tte_embed, but also copies the residual stream after the embedding
  * LayerNorm and after each of the first n_dump layers into
- * d_states (fp32 [n_dump + 1, n_tokens, H]).  If n_dump < n_layers the pass
+ * d_states (fp32 [n_dump + 1, n_tokens, H]; in TTE_BF16 the bf16 stream's
+ * values, exactly).  If n_dump < n_layers the pass
  * stops there and d_out is not written (it may be NULL). */
 tte_status tte_embed_trace(tte_model* m, const int32_t* d_token_ids, int32_t n_tokens,
                            const int32_t* h_offsets, int32_t n_texts, float* d_out,
@@ -267,7 +269,10 @@ typedef enum { TTE_EPI_STORE = 0, TTE_EPI_RESIDUAL = 1, TTE_EPI_GEGLU = 2 } tte_
  * int32 block product and S the block sum of the activation codes; K a
  * multiple of 256).
  * epilogue: STORE writes d_c [M, N] (fp32, or bf16 if out_kind is BF16);
- * RESIDUAL adds into fp32 d_c [M, N]; GEGLU takes W with 2N rows and writes
+ * RESIDUAL adds into fp32 d_c [M, N], or with TTE_BF16 and out_kind BF16
+ * into bf16 d_c (the sum taken in fp32 and rounded once to nearest even;
+ * out_kind BF16 with another precision is TTE_E_INVALID); GEGLU takes W
+ * with 2N rows and writes
  * d_c[m, n] = GELU(y[m, n]) * y[m, N + n] (erf GELU). */
 tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, const float* d_a_scale,
                        const void* d_w, const float* d_w_scale, int32_t M, int32_t N, int32_t K,

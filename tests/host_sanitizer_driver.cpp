@@ -173,6 +173,10 @@ static void op_refusals() {
          TTE_E_UNSUPPORTED);
   EXPECT(tte_op_gemm(TTE_INT8, TTE_EPI_RESIDUAL, nullptr, nullptr, nullptr, nullptr, 16, 128, 128, nullptr, 1,
                      nullptr) == TTE_E_INVALID);
+  EXPECT(tte_op_gemm(TTE_FP32, TTE_EPI_RESIDUAL, nullptr, nullptr, nullptr, nullptr, 16, 128, 128, nullptr, 1,
+                     nullptr) == TTE_E_INVALID);
+  EXPECT(tte_op_gemm(TTE_BF16, TTE_EPI_RESIDUAL, nullptr, nullptr, nullptr, nullptr, 0, 128, 128, nullptr, 1,
+                     nullptr) == TTE_OK);
   EXPECT(tte_op_gemm_splitk(TTE_BF16, nullptr, nullptr, nullptr, nullptr, 16, 128, 320, 2, nullptr, nullptr) ==
          TTE_E_UNSUPPORTED);
   EXPECT(tte_op_gemm_splitk(TTE_BF16, nullptr, nullptr, nullptr, nullptr, 16, 128, 512, 0, nullptr, nullptr) ==

@@ -169,6 +169,49 @@ def encode_layers_fp32_rounded(cfg, w, ids, offsets):
     return states
 
 
+def encode_layers_bf16_emulated(cfg, w, ids, offsets, stream_bf16=True):
+    """The oracle's bf16 pass (tensai page, section 何が動くか, encoder
+    paragraph) composed from its own functions, with the bf16 roundings of
+    the kernels' data flow applied between steps: every weight-product and
+    attention operand rounded to bf16 (norm outputs, Q/K/V, attention output,
+    GeGLU output) and, with stream_bf16, the residual stream rounded to bf16
+    after the embedding norm and after each of its updates (the update
+    itself added exactly, as the kernels add it in fp32 and round once).
+    Attention's internal roundings are left out (their own bound is
+    attention_bf16_bound).  Returns the residual states after the embedding
+    norm and after each layer."""
+    from oracle import encoder as E
+    nh, d, prec = cfg["heads"], cfg["head_dim"], cfg["precision"]
+    rx = bf16_round if stream_bf16 else (lambda v: np.asarray(v, np.float64))
+    emb = E.decode_matrix(w, "tok_emb", prec)
+    off = E.validate_offsets(offsets, len(ids))
+    x = rx(E.layer_norm(emb[np.asarray(ids, np.int64)], w["emb_norm"], cfg["ln_eps"]))
+    states = [x]
+    for l in range(cfg["layers"]):
+        layer = w["layers"][l]
+        g = (l % cfg["global_every"]) == 0
+        base = cfg["rope_base_global"] if g else cfg["rope_base_local"]
+        a = x if l == 0 else E.layer_norm(x, layer["attn_norm"], cfg["ln_eps"])
+        qkv = bf16_round(E._project(bf16_round(a), layer, "wqkv", prec))
+        o = E.attention(qkv, off, nh, d, g, cfg["window"], base)
+        x = rx(x + E._project(bf16_round(o), layer, "wo", prec))
+        m = E.layer_norm(x, layer["mlp_norm"], cfg["ln_eps"])
+        y = E.geglu(E._project(bf16_round(m), layer, "wi", prec))
+        x = rx(x + E._project(bf16_round(y), layer, "wo2", prec))
+        states.append(x)
+    return states
+
+
+def pooled_spread(cfg, w, ids, offsets, states):
+    """1 - min and 1 - mean over texts of the cosine between the oracle's
+    pooled vectors and those pooled from `states[-1]`."""
+    from oracle import encoder as E
+    ref = oracle.encode(cfg, w, ids, offsets)
+    got = E.mean_pool_l2(E.layer_norm(states[-1], w["final_norm"], cfg["ln_eps"]), offsets)
+    c = cos_rows(ref, got)
+    return 1 - c.min(), 1 - c.mean()
+
+
 def cos_rows(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)

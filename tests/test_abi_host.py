@@ -109,6 +109,11 @@ def test_op_gemm_shape_checks_need_no_gpu(lib):
     assert st == B.TTE_E_UNSUPPORTED
     st = lib.tte_op_gemm(B.TTE_INT8, B.TTE_EPI_RESIDUAL, None, None, None, None, 16, 128, 128, None, 1, None)
     assert st == B.TTE_E_INVALID
+    st = lib.tte_op_gemm(B.TTE_FP32, B.TTE_EPI_RESIDUAL, None, None, None, None, 16, 128, 128, None, 1, None)
+    assert st == B.TTE_E_INVALID
+    # a bf16 residual stream is accepted with bf16 operands (M = 0: no launch)
+    st = lib.tte_op_gemm(B.TTE_BF16, B.TTE_EPI_RESIDUAL, None, None, None, None, 0, 128, 128, None, 1, None)
+    assert st == B.TTE_OK
     # split-K: K must divide into parts of whole 128-byte chunks
     st = lib.tte_op_gemm_splitk(B.TTE_BF16, None, None, None, None, 16, 128, 320, 2, None, None)
     assert st == B.TTE_E_UNSUPPORTED

@@ -160,6 +160,20 @@ def test_gemm_bf16(M, N, K):
     cr = dev(r)
     _run_gemm(B.TTE_BF16, B.TTE_EPI_RESIDUAL, da, None, dw, None, M, N, K, cr, B.TTE_OUT_F32)
     np.testing.assert_allclose(host(cr), r + ref, atol=2e-5, rtol=1e-5)
+    # bf16 residual stream: x + A W^T summed in fp32 and rounded once to
+    # bf16, so within half a bf16 ulp (at most 2^-8 of the value: 8
+    # significant bits) of the exact sum plus
+    # the fp32 product's error, and equal to the exact sum's rounding except
+    # where that error crosses a rounding boundary
+    rb = ti.bf16_bits(r)
+    want = ti.bf16_to_f32(rb).astype(np.float64) + ref
+    crb = dev(rb)
+    _run_gemm(B.TTE_BF16, B.TTE_EPI_RESIDUAL, da, None, dw, None, M, N, K, crb, B.TTE_OUT_BF16)
+    got = ti.bf16_to_f32(host(crb).view(np.uint16)).astype(np.float64)
+    np.testing.assert_allclose(got, want, atol=2e-5, rtol=2.0 ** -8)
+    same = got == ti.bf16_to_f32(ti.bf16_bits(want.astype(np.float32))).astype(np.float64)
+    say(f"  bf16 residual: {same.mean():.5f} of elements equal the exact sum's rounding")
+    assert same.mean() > 0.99
 
 
 @pytest.mark.parametrize("M,N,K", SHAPES)

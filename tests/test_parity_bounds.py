@@ -17,8 +17,8 @@ import pytest
 
 import oracle
 import tte_inputs as ti
-from parity_bounds import (attention_bf16_bound, attention_bf16_emulated, cos_rows, encode_layers_fp32_rounded,
-                           rounding_spread)
+from parity_bounds import (attention_bf16_bound, attention_bf16_emulated, cos_rows, encode_layers_bf16_emulated,
+                           encode_layers_fp32_rounded, pooled_spread, rounding_spread)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -122,3 +122,23 @@ def test_stored_spreads_back_the_integer_gate(name):
     assert 1 - 0.998 >= 1.5 * fin_min and 1 - 0.999 >= 1.5 * fin_mean
     # the spread only grows with depth (up to small wiggles)
     assert np.all(np.diff(per_min[1:]) > -0.1 * per_min[1:-1])
+
+
+def test_bf16_stream_rounding_sits_well_inside_the_bf16_gate():
+    """Three texts (491 tokens) of the full-size bf16 workload's first pack,
+    25 layers, on the CPU: the kernels' bf16 operand roundings with the
+    residual stream also held in bf16 end at pooled 1 - cos of order 1e-4
+    at most, a tenth of what the end-to-end gate (min cos >= 0.999) allows;
+    holding the stream in bf16 really moves the result (several times the
+    spread of the operand roundings alone)."""
+    cfg = ti.workload("full_bf16_packs2048")["cfg"]
+    w = ti.cached_storage_weights(cfg)
+    pack = _subpack("full_bf16_packs2048", 0, range(3))
+    c = cfg.as_dict()
+    ops_only = pooled_spread(c, w, pack.ids, pack.offsets,
+                             encode_layers_bf16_emulated(c, w, pack.ids, pack.offsets, stream_bf16=False))
+    stream = pooled_spread(c, w, pack.ids, pack.offsets, encode_layers_bf16_emulated(c, w, pack.ids, pack.offsets))
+    print(f"bf16 operands: 1 - cos min {ops_only[0]:.2e} mean {ops_only[1]:.2e}; "
+          f"+ bf16 stream: {stream[0]:.2e} / {stream[1]:.2e}")
+    assert stream[0] < 0.1 * (1 - 0.999)
+    assert stream[0] > 2 * ops_only[0]

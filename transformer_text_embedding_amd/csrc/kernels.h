@@ -56,16 +56,22 @@ struct PackIO {
 // width/64 in this set.
 bool row_width_supported(int width);
 
+// The residual stream x [T, H] is fp32 (x_kind O_F32), or bf16 (O_BF16)
+// in the bf16 mode; its updates are added in fp32 and rounded once when
+// stored.
+
 // Gather rows of the token table (fp32, bf16, or int8 blocks with fp32
-// scales), bias-free LayerNorm with gain `gamma`, write fp32 x [T, H].
-// Also writes seg[t] from the device copy of the offsets.
+// scales), bias-free LayerNorm with gain `gamma`, write x [T, H] (bf16 x
+// with a bf16 table only).  Also writes seg[t] from the device copy of the
+// offsets.
 void launch_embed_ln(int prec, const int32_t* ids, const PackIO* io, int T, const void* table,
                      const float* table_scale, int vocab, const float* gamma, float eps, int H, const int* d_off,
-                     int n_texts, float* x, Seg* seg, hipStream_t s);
+                     int n_texts, void* x, int x_kind, Seg* seg, hipStream_t s);
 
 // Bias-free LayerNorm (gamma non-null) or plain conversion (gamma null) of
-// fp32 rows to fp32 / bf16 / 7-bit int8 codes + row scales.
-void launch_ln(const float* x, const float* gamma, int rows, int width, float eps, int out_kind, void* out,
+// fp32 rows to fp32 / bf16 / 7-bit int8 codes + row scales; of bf16 rows
+// to fp32 / bf16.
+void launch_ln(const void* x, int x_kind, const float* gamma, int rows, int width, float eps, int out_kind, void* out,
                float* out_scale, hipStream_t s, const PackIO* io = nullptr);
 
 // Per-row 7-bit quantisation.
@@ -95,7 +101,9 @@ inline void launch_timed(void (*kernel)(KArgs...), dim3 grid, dim3 block, uint32
 }
 
 // C = A * W^T with epilogue; see tte_op_gemm.  Requires N % 128 == 0
-// (GEGLU: N % 64 == 0) and K % 128 == 0.
+// (GEGLU: N % 64 == 0) and K % 128 == 0.  E_RESID adds into fp32 C, or,
+// for bf16 operands with out_kind O_BF16, into bf16 C (the sum taken in
+// fp32, rounded once).
 void launch_gemm(int prec, int epi, const void* A, const float* a_scale, const void* W, const float* w_scale,
                  int M, int N, int K, void* C, int out_kind, hipStream_t s);
 
@@ -114,9 +122,10 @@ int residual_splits(int prec, int M, int N, int K, int max_splits);
 // x += partials[0] + ... + partials[splits-1] (in that order), then the
 // bias-free LayerNorm (gamma non-null) or plain conversion (gamma null) of
 // the new x to out (fp32 / bf16 / 7-bit codes + scales), or no output
-// (out_kind < 0).  One wave per row.
-void launch_resid_ln(float* x, const float* partials, int splits, const float* gamma, int rows, int width, float eps,
-                     int out_kind, void* out, float* out_scale, hipStream_t s);
+// (out_kind < 0).  bf16 x: the update alone, or with the norm into bf16.
+// One wave per row.
+void launch_resid_ln(void* x, int x_kind, const float* partials, int splits, const float* gamma, int rows, int width,
+                     float eps, int out_kind, void* out, float* out_scale, hipStream_t s);
 
 // QKV projection with the RoPE / transposed-V epilogue: writes rotated Q
 // and K into qkv [M, 3H] (columns 0 .. 2H-1) and V into qo.vt.  Requires
@@ -147,7 +156,7 @@ void launch_similarity(const float* e, int n, int dim, float* sim, hipStream_t s
 // Final LayerNorm + mean per text + L2.  Units of up to POOL_ROWS rows of
 // one text: unit_start[b] .. unit_start[b+1] belong to text b.
 constexpr int POOL_ROWS = 32;
-void launch_pool(const float* x, const float* gamma, float eps, int H, const int* d_off, const int* d_unit,
+void launch_pool(const void* x, int x_kind, const float* gamma, float eps, int H, const int* d_off, const int* d_unit,
                  int n_texts, int n_units, float* partial, float* out, hipStream_t s, const PackIO* io = nullptr);
 
 }  // namespace tte

@@ -161,6 +161,38 @@ __device__ __forceinline__ long unpack_q4(uint32_t x) {
   return (long)(((uint64_t)b << 32) | a);
 }
 
+// One 4-column chunk of the residual stream x [M, N] as the residual
+// epilogue reads and writes it: fp32 (16 bytes), or bf16 (8 bytes; the
+// fp32 sum is rounded once, to nearest even).  Rows at or past M read as 0.
+template <bool XB>
+struct XChunk {
+  using type = f32x4;
+  __device__ static __forceinline__ f32x4 load(const void* C, int m, int M, int N, int n) {
+    return m < M ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(C) + (size_t)m * N + n)
+                 : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  __device__ static __forceinline__ f32x4 widen(f32x4 v) { return v; }
+  __device__ static __forceinline__ void store(void* C, int m, int N, int n, f32x4 v) {
+    *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + (size_t)m * N + n) = v;
+  }
+};
+template <>
+struct XChunk<true> {
+  using type = u32x2;
+  __device__ static __forceinline__ u32x2 load(const void* C, int m, int M, int N, int n) {
+    return m < M ? *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(C) + (size_t)m * N + n)
+                 : u32x2{0u, 0u};
+  }
+  __device__ static __forceinline__ f32x4 widen(u32x2 v) {
+    return f32x4{__uint_as_float(v[0] << 16), __uint_as_float(v[0] & 0xFFFF0000u), __uint_as_float(v[1] << 16),
+                 __uint_as_float(v[1] & 0xFFFF0000u)};
+  }
+  __device__ static __forceinline__ void store(void* C, int m, int N, int n, f32x4 v) {
+    *reinterpret_cast<u32x2*>(reinterpret_cast<uint16_t*>(C) + (size_t)m * N + n) =
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+};
+
 template <int PREC, int EPI, int OUT, int WM, int WN, int STAGES, int WGM, int WGN, int KT>
 // The 128 x 192 bf16 GeGLU tiles (32 x 96 waves) are held to 4 waves per
 // SIMD, 128 registers, so that two blocks share a CU (the compiler spills
@@ -252,25 +284,26 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
     s_src = w_scale + (size_t)w_row<EPI, BN, WGN>(wid * 32 + (lane & 31), nb, N) * (K / 32) + split * (k_part / 32);
 
   // bf16 residual products in tiles of at most 8 MFMA tiles per wave (32
-  // more registers; larger wave tiles would spill): the x values this lane
-  // adds in the epilogue (its WN 16-byte chunks of each of its WM 16-row
-  // slabs, in the epilogue's lane order) are loaded before the K loop, so
-  // their latency overlaps the loop instead of following it.  No block
-  // writes another block's part of x, and the loop's waits for its own
-  // (younger) tile loads also cover these.
+  // more registers with fp32 x, 16 with bf16 x; larger wave tiles would
+  // spill): the x values this lane adds in the epilogue (its WN 4-column
+  // chunks of each of its WM 16-row slabs, in the epilogue's lane order)
+  // are loaded before the K loop, so their latency overlaps the loop
+  // instead of following it.  No block writes another block's part of x,
+  // and the loop's waits for its own (younger) tile loads also cover these.
+  constexpr bool XB = EPI == E_RESID && OUT == O_BF16;  // bf16 residual stream
+  using XC = typename XChunk<XB>::type;
   constexpr bool XPRE = EPI == E_RESID && PREC == P_BF16 && WM * WN <= 8;
-  f32x4 xpre[XPRE ? WM : 1][XPRE ? WN : 1];
+  XC xpre[XPRE ? WM : 1][XPRE ? WN : 1];
   if constexpr (XPRE) {
-    constexpr int XCPR = 4 * WN;  // 16-byte chunks of a wave's 16 WN fp32 columns
+    constexpr int XCPR = 4 * WN;  // 4-column chunks of a wave's 16 WN columns
     const int n_wave = nb * BN + wn * 16 * WN;
 #pragma unroll
     for (int mt = 0; mt < WM; ++mt) {
       const int m_slab = m0 + wm * 16 * WM + mt * 16;
 #pragma unroll
       for (int i = 0; i < WN; ++i) {
-        const int c = lane + 64 * i, row = c / XCPR, cc = c % XCPR, m = m_slab + row;
-        xpre[mt][i] = m < M ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(C) + (size_t)m * N + n_wave + 4 * cc)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
+        const int c = lane + 64 * i, row = c / XCPR, cc = c % XCPR;
+        xpre[mt][i] = XChunk<XB>::load(C, m_slab + row, M, N, n_wave + 4 * cc);
       }
     }
     asm volatile("" ::: "memory");  // issued here, ahead of the first K tiles
@@ -670,20 +703,19 @@ __global__ __launch_bounds__(64 * WGM * WGN) __attribute__((amdgpu_waves_per_eu(
       constexpr int NI = 16 * CPR / 64;
       static_assert(NI * 64 == 16 * CPR, "whole chunks per lane");
       static_assert(!XPRE || NI == WN, "the prefetched chunks are the epilogue's");
-      f32x4 ov[NI], dv[NI];
+      XC ov[NI];
+      f32x4 dv[NI];
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
-        const int c = lane + 64 * i, row = c / CPR, cc = c % CPR, m = m_slab + row;
+        const int c = lane + 64 * i, row = c / CPR, cc = c % CPR;
         dv[i] = *reinterpret_cast<const f32x4*>(slab + row * RB + cc * 16);
         if constexpr (XPRE) ov[i] = xpre[mt][i];
-        else
-          ov[i] = m < M ? *reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(C) + (size_t)m * N + n_wave + 4 * cc)
-                        : f32x4{0.f, 0.f, 0.f, 0.f};
+        else ov[i] = XChunk<XB>::load(C, m_slab + row, M, N, n_wave + 4 * cc);
       }
 #pragma unroll
       for (int i = 0; i < NI; ++i) {
         const int c = lane + 64 * i, row = c / CPR, cc = c % CPR, m = m_slab + row;
-        if (m < M) *reinterpret_cast<f32x4*>(reinterpret_cast<float*>(C) + (size_t)m * N + n_wave + 4 * cc) = ov[i] + dv[i];
+        if (m < M) XChunk<XB>::store(C, m, N, n_wave + 4 * cc, XChunk<XB>::widen(ov[i]) + dv[i]);
       }
       __builtin_amdgcn_wave_barrier();
       continue;
@@ -731,6 +763,12 @@ template <int PREC, int WM, int ST, int WGM = 2, int WGN = 2, int KT = 128, int 
 void go_prec(int epi, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int N, int K,
              void* C, int out_kind, hipStream_t s) {
   if (epi == E_RESID) {
+    if constexpr (PREC == P_BF16) {
+      if (out_kind == O_BF16) {
+        go<PREC, E_RESID, O_BF16, WM, WN, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
+        return;
+      }
+    }
     go<PREC, E_RESID, O_F32, WM, WN, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);
   } else if (epi == E_GEGLU) {
     if (out_kind == O_BF16) go<PREC, E_GEGLU, O_BF16, WM, WN, ST, WGM, WGN, KT>(A, a_scale, W, w_scale, M, N, K, C, s);

@@ -72,6 +72,43 @@ __device__ __forceinline__ void store_bf16_row(uint16_t* __restrict__ row, int l
   }
 }
 
+template <int EPL>
+__device__ __forceinline__ void load_bf16_row(const uint16_t* __restrict__ row, int lane, float (&v)[EPL]) {
+  using RS = RowShape<EPL>;
+#pragma unroll
+  for (int c = 0; c < RS::CH; ++c) {
+    const uint16_t* p = row + RS::col(c, lane, 0);
+    if constexpr (RS::VEC == 4) {
+      const u16x4 t = *reinterpret_cast<const u16x4*>(p);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) v[c * 4 + e] = bf16_to_f32(t[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < RS::VEC; ++e) v[c * RS::VEC + e] = bf16_to_f32(p[e]);
+    }
+  }
+}
+
+// Row r of the residual stream x: fp32, or bf16 (XB) in the bf16 mode.
+template <int EPL, bool XB>
+__device__ __forceinline__ void load_x_row(const void* __restrict__ x, size_t r, int lane, float (&v)[EPL]) {
+  if constexpr (XB) load_bf16_row<EPL>(reinterpret_cast<const uint16_t*>(x) + r * RowShape<EPL>::W, lane, v);
+  else load_f32_row<EPL>(reinterpret_cast<const float*>(x) + r * RowShape<EPL>::W, lane, v);
+}
+
+// Stores row r of x; with XB the values are first rounded to bf16 in
+// place, so that what the caller goes on to use is what x now holds.
+template <int EPL, bool XB>
+__device__ __forceinline__ void store_x_row(void* __restrict__ x, size_t r, int lane, float (&v)[EPL]) {
+  if constexpr (XB) {
+#pragma unroll
+    for (int i = 0; i < EPL; ++i) v[i] = bf16_to_f32(f32_to_bf16(v[i]));
+    store_bf16_row<EPL>(reinterpret_cast<uint16_t*>(x) + r * RowShape<EPL>::W, lane, v);
+  } else {
+    store_f32_row<EPL>(reinterpret_cast<float*>(x) + r * RowShape<EPL>::W, lane, v);
+  }
+}
+
 // 7-bit codes of a row held in registers; returns the row scale amax/63.
 template <int EPL>
 __device__ __forceinline__ float store_q7_row(int8_t* __restrict__ row, int lane, const float (&v)[EPL]) {
@@ -124,13 +161,13 @@ __device__ __forceinline__ void layernorm_regs(float (&v)[EPL], const float* __r
 // embedding gather + LayerNorm; per-token text bounds
 // --------------------------------------------------------------------------
 
-template <int EPL, int PREC>
+template <int EPL, int PREC, bool XB>
 __global__ __launch_bounds__(256) void k_embed_ln(const int32_t* __restrict__ ids, const PackIO* __restrict__ io,
                                                   int T, const void* __restrict__ table,
                                                   const float* __restrict__ table_scale, int vocab,
                                                   const float* __restrict__ gamma, float eps,
                                                   const int* __restrict__ off, int n_texts,
-                                                  float* __restrict__ x, Seg* __restrict__ seg) {
+                                                  void* __restrict__ x, Seg* __restrict__ seg) {
   using RS = RowShape<EPL>;
   constexpr int H = RS::W;
   const int lane = threadIdx.x & 63;
@@ -161,16 +198,16 @@ __global__ __launch_bounds__(256) void k_embed_ln(const int32_t* __restrict__ id
       }
   }
   layernorm_regs<EPL>(v, gamma, lane, eps);
-  store_f32_row<EPL>(x + (size_t)t * H, lane, v);
+  store_x_row<EPL, XB>(x, (size_t)t, lane, v);
   if (lane == 0) seg[t] = Seg{off[b], off[b + 1]};
 }
 
 // --------------------------------------------------------------------------
-// LayerNorm / conversion / quantisation of fp32 rows
+// LayerNorm / conversion / quantisation of fp32 (or, XB, bf16) rows
 // --------------------------------------------------------------------------
 
-template <int EPL, int OUT, bool NORM>
-__global__ __launch_bounds__(256) void k_ln(const float* __restrict__ x, const float* __restrict__ gamma, int rows,
+template <int EPL, int OUT, bool NORM, bool XB>
+__global__ __launch_bounds__(256) void k_ln(const void* __restrict__ x, const float* __restrict__ gamma, int rows,
                                             float eps, void* __restrict__ out, float* __restrict__ out_scale,
                                             const PackIO* __restrict__ io) {
   using RS = RowShape<EPL>;
@@ -180,7 +217,7 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ x, const f
   if (r >= rows) return;
   if (io) out = io->out;
   float v[EPL];
-  load_f32_row<EPL>(x + (size_t)r * Wd, lane, v);
+  load_x_row<EPL, XB>(x, (size_t)r, lane, v);
   if constexpr (NORM) layernorm_regs<EPL>(v, gamma, lane, eps);
   if constexpr (OUT == O_F32) {
     store_f32_row<EPL>(reinterpret_cast<float*>(out) + (size_t)r * Wd, lane, v);
@@ -196,11 +233,12 @@ __global__ __launch_bounds__(256) void k_ln(const float* __restrict__ x, const f
 // residual update from split-K partial products, fused with the next norm
 // --------------------------------------------------------------------------
 
-// x[r] += p_0[r] + ... + p_{S-1}[r] (in split order), written back; then
-// LayerNorm / conversion / quantisation of the updated row into out
-// (WRITE = false: the residual update only).
-template <int EPL, int OUT, bool NORM, bool WRITE>
-__global__ __launch_bounds__(256) void k_resid_ln(float* __restrict__ x, const float* __restrict__ partials,
+// x[r] += p_0[r] + ... + p_{S-1}[r] (in split order, in fp32), written back
+// (rounded to bf16 with XB); then LayerNorm / conversion / quantisation of
+// the updated row, as x now holds it, into out (WRITE = false: the
+// residual update only).
+template <int EPL, int OUT, bool NORM, bool WRITE, bool XB>
+__global__ __launch_bounds__(256) void k_resid_ln(void* __restrict__ x, const float* __restrict__ partials,
                                                   int splits, const float* __restrict__ gamma, int rows, float eps,
                                                   void* __restrict__ out, float* __restrict__ out_scale) {
   using RS = RowShape<EPL>;
@@ -209,7 +247,7 @@ __global__ __launch_bounds__(256) void k_resid_ln(float* __restrict__ x, const f
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= rows) return;
   float v[EPL];
-  load_f32_row<EPL>(x + (size_t)r * Wd, lane, v);
+  load_x_row<EPL, XB>(x, (size_t)r, lane, v);
   // up to 4 partial rows in flight at once, added in split order
   for (int sp0 = 0; sp0 < splits; sp0 += 4) {
     float p[4][EPL];
@@ -223,7 +261,7 @@ __global__ __launch_bounds__(256) void k_resid_ln(float* __restrict__ x, const f
         for (int i = 0; i < EPL; ++i) v[i] += p[j][i];
       }
   }
-  store_f32_row<EPL>(x + (size_t)r * Wd, lane, v);
+  store_x_row<EPL, XB>(x, (size_t)r, lane, v);
   if constexpr (WRITE) {
     if constexpr (NORM) layernorm_regs<EPL>(v, gamma, lane, eps);
     if constexpr (OUT == O_F32) {
@@ -244,8 +282,8 @@ __global__ __launch_bounds__(256) void k_resid_ln(float* __restrict__ x, const f
 // Stage 1: one block per unit (up to POOL_ROWS rows of one text): LayerNorm
 // of each row in registers, per-wave column sums, then a fixed-order sum of
 // the 4 waves through LDS -> partial[u, :].  No atomics: deterministic.
-template <int EPL>
-__global__ __launch_bounds__(256) void k_pool_partial(const float* __restrict__ x, const float* __restrict__ gamma,
+template <int EPL, bool XB>
+__global__ __launch_bounds__(256) void k_pool_partial(const void* __restrict__ x, const float* __restrict__ gamma,
                                                       float eps, const int* __restrict__ off,
                                                       const int* __restrict__ unit_start, int n_texts,
                                                       float* __restrict__ partial) {
@@ -267,7 +305,7 @@ __global__ __launch_bounds__(256) void k_pool_partial(const float* __restrict__ 
     float v[RB][EPL];
 #pragma unroll
     for (int k = 0; k < RB; ++k)
-      if (rb + 4 * k < r1) load_f32_row<EPL>(x + (size_t)(rb + 4 * k) * H, lane, v[k]);
+      if (rb + 4 * k < r1) load_x_row<EPL, XB>(x, (size_t)(rb + 4 * k), lane, v[k]);
 #pragma unroll
     for (int k = 0; k < RB; ++k) {
       if (rb + 4 * k < r1) {  // wave-uniform
@@ -358,77 +396,96 @@ bool row_width_supported(int width) {
   }
 
 void launch_embed_ln(int prec, const int32_t* ids, const PackIO* io, int T, const void* table, const float* table_scale,
-                     int vocab, const float* gamma, float eps, int H, const int* d_off, int n_texts, float* x, Seg* seg,
-                     hipStream_t s) {
+                     int vocab, const float* gamma, float eps, int H, const int* d_off, int n_texts, void* x,
+                     int x_kind, Seg* seg, hipStream_t s) {
   if (T <= 0) return;
   const dim3 grid((T + 3) / 4), block(256);
-#define L_EMB(E)                                                                                                    \
-  if (prec == P_F32)                                                                                                \
-    launch_timed(k_embed_ln<E, P_F32>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, \
-                                                 x, seg);                                                           \
-  else if (prec == P_BF16)                                                                                          \
-    launch_timed(k_embed_ln<E, P_BF16>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, \
-                                                  x, seg);                                                          \
-  else                                                                                                              \
-    launch_timed(k_embed_ln<E, P_I8>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps, d_off, n_texts, x, \
-                                                seg);
+#define L_EMB(E)                                                                                                      \
+  if (prec == P_F32)                                                                                                  \
+    launch_timed(k_embed_ln<E, P_F32, false>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps,   \
+                 d_off, n_texts, x, seg);                                                                             \
+  else if (prec == P_BF16 && x_kind == O_BF16)                                                                        \
+    launch_timed(k_embed_ln<E, P_BF16, true>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps,   \
+                 d_off, n_texts, x, seg);                                                                             \
+  else if (prec == P_BF16)                                                                                            \
+    launch_timed(k_embed_ln<E, P_BF16, false>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps,  \
+                 d_off, n_texts, x, seg);                                                                             \
+  else                                                                                                                \
+    launch_timed(k_embed_ln<E, P_I8, false>, grid, block, 0, s, ids, io, T, table, table_scale, vocab, gamma, eps,    \
+                 d_off, n_texts, x, seg);
   TTE_EPL_DISPATCH(H, L_EMB)
 #undef L_EMB
 }
 
-void launch_ln(const float* x, const float* gamma, int rows, int width, float eps, int out_kind, void* out,
+// fp32 x: every output form, with or without the norm; bf16 x: fp32 and
+// bf16 outputs only (the bf16 mode has no 7-bit codes).
+void launch_ln(const void* x, int x_kind, const float* gamma, int rows, int width, float eps, int out_kind, void* out,
                float* out_scale, hipStream_t s, const PackIO* io) {
   if (rows <= 0) return;
   const dim3 grid((rows + 3) / 4), block(256);
-#define L_LN(E)                                                                                        \
-  if (gamma) {                                                                                         \
-    if (out_kind == O_F32) launch_timed(k_ln<E, O_F32, true>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);   \
-    else if (out_kind == O_BF16) launch_timed(k_ln<E, O_BF16, true>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io); \
-    else launch_timed(k_ln<E, O_I8, true>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);              \
-  } else {                                                                                             \
-    if (out_kind == O_F32) launch_timed(k_ln<E, O_F32, false>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);  \
-    else if (out_kind == O_BF16) launch_timed(k_ln<E, O_BF16, false>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io); \
-    else launch_timed(k_ln<E, O_I8, false>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);             \
+#define L_LN_X(E, NORM)                                                                                              \
+  if (x_kind == O_BF16) {                                                                                            \
+    if (out_kind == O_F32)                                                                                           \
+      launch_timed(k_ln<E, O_F32, NORM, true>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);          \
+    else if (out_kind == O_BF16)                                                                                     \
+      launch_timed(k_ln<E, O_BF16, NORM, true>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);         \
+  } else if (out_kind == O_F32) {                                                                                    \
+    launch_timed(k_ln<E, O_F32, NORM, false>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);           \
+  } else if (out_kind == O_BF16) {                                                                                   \
+    launch_timed(k_ln<E, O_BF16, NORM, false>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);          \
+  } else {                                                                                                           \
+    launch_timed(k_ln<E, O_I8, NORM, false>, grid, block, 0, s, x, gamma, rows, eps, out, out_scale, io);            \
+  }
+#define L_LN(E)           \
+  if (gamma) {            \
+    L_LN_X(E, true)       \
+  } else {                \
+    L_LN_X(E, false)      \
   }
   TTE_EPL_DISPATCH(width, L_LN)
 #undef L_LN
+#undef L_LN_X
 }
 
 void launch_quant7(const float* x, int rows, int width, int8_t* q, float* scale, hipStream_t s) {
-  launch_ln(x, nullptr, rows, width, 0.f, O_I8, q, scale, s);
+  launch_ln(x, O_F32, nullptr, rows, width, 0.f, O_I8, q, scale, s);
 }
 
-void launch_resid_ln(float* x, const float* partials, int splits, const float* gamma, int rows, int width, float eps,
-                     int out_kind, void* out, float* out_scale, hipStream_t s) {
+// fp32 x: the update alone or with any output form; bf16 x: the update
+// alone, or with the norm into bf16 (the forms the bf16 mode runs).
+void launch_resid_ln(void* x, int x_kind, const float* partials, int splits, const float* gamma, int rows, int width,
+                     float eps, int out_kind, void* out, float* out_scale, hipStream_t s) {
   if (rows <= 0) return;
   const dim3 grid((rows + 3) / 4), block(256);
-#define L_RLN(E)                                                                                                      \
-  if (out_kind < 0) {                                                                                                 \
-    launch_timed(k_resid_ln<E, O_F32, false, false>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);  \
-  } else if (gamma) {                                                                                                 \
-    if (out_kind == O_F32)                                                                                            \
-      launch_timed(k_resid_ln<E, O_F32, true, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);  \
-    else if (out_kind == O_BF16)                                                                                      \
-      launch_timed(k_resid_ln<E, O_BF16, true, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale); \
-    else                                                                                                              \
-      launch_timed(k_resid_ln<E, O_I8, true, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);   \
-  } else {                                                                                                            \
-    if (out_kind == O_F32)                                                                                            \
-      launch_timed(k_resid_ln<E, O_F32, false, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale); \
-    else if (out_kind == O_BF16)                                                                                      \
-      launch_timed(k_resid_ln<E, O_BF16, false, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);\
-    else                                                                                                              \
-      launch_timed(k_resid_ln<E, O_I8, false, true>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, out_scale);  \
+#define RLN(E, OUT, NORM, WRITE, XB)                                                                               \
+  launch_timed(k_resid_ln<E, OUT, NORM, WRITE, XB>, grid, block, 0, s, x, partials, splits, gamma, rows, eps, out, \
+               out_scale)
+#define L_RLN(E)                                                                     \
+  if (x_kind == O_BF16) {                                                            \
+    if (out_kind < 0) RLN(E, O_F32, false, false, true);                             \
+    else if (gamma && out_kind == O_BF16) RLN(E, O_BF16, true, true, true);          \
+  } else if (out_kind < 0) {                                                         \
+    RLN(E, O_F32, false, false, false);                                              \
+  } else if (gamma) {                                                                \
+    if (out_kind == O_F32) RLN(E, O_F32, true, true, false);                         \
+    else if (out_kind == O_BF16) RLN(E, O_BF16, true, true, false);                  \
+    else RLN(E, O_I8, true, true, false);                                            \
+  } else {                                                                           \
+    if (out_kind == O_F32) RLN(E, O_F32, false, true, false);                        \
+    else if (out_kind == O_BF16) RLN(E, O_BF16, false, true, false);                 \
+    else RLN(E, O_I8, false, true, false);                                           \
   }
   TTE_EPL_DISPATCH(width, L_RLN)
 #undef L_RLN
+#undef RLN
 }
 
-void launch_pool(const float* x, const float* gamma, float eps, int H, const int* d_off, const int* d_unit,
+void launch_pool(const void* x, int x_kind, const float* gamma, float eps, int H, const int* d_off, const int* d_unit,
                  int n_texts, int n_units, float* partial, float* out, hipStream_t s, const PackIO* io) {
   if (n_texts <= 0) return;
 #define L_POOL(E)                                                                                          \
-  k_pool_partial<E><<<n_units, 256, 0, s>>>(x, gamma, eps, d_off, d_unit, n_texts, partial);               \
+  if (x_kind == O_BF16) k_pool_partial<E, true><<<n_units, 256, 0, s>>>(x, gamma, eps, d_off, d_unit, n_texts, partial); \
+  else k_pool_partial<E, false><<<n_units, 256, 0, s>>>(x, gamma, eps, d_off, d_unit, n_texts, partial);   \
   k_pool_finish<E * 64><<<n_texts, 256, 0, s>>>(partial, d_off, d_unit, out, io);
   TTE_EPL_DISPATCH(H, L_POOL)
 #undef L_POOL

@@ -84,6 +84,10 @@ struct Layout {
 
 int act_bytes(int prec) { return prec == TTE_BF16 ? 2 : 4; }
 
+// The residual stream is held in bf16 in the bf16 mode (every update is
+// added in fp32 and rounded once), in fp32 otherwise.
+int x_kind(int prec) { return prec == TTE_BF16 ? O_BF16 : O_F32; }
+
 Layout layout_of(const tte_config& c) {
   Layout L{};
   const size_t T = (size_t)c.max_tokens, H = (size_t)c.hidden, I = (size_t)c.intermediate;
@@ -100,7 +104,7 @@ Layout layout_of(const tte_config& c) {
     }
     return at;
   };
-  L.x = take(T * H * 4);
+  L.x = take(T * H * ab);  // the residual stream: bf16 in the bf16 mode, else fp32
   L.xa = take(c.precision >= TTE_INT8 ? T * (H > I ? H : I) : T * H * ab);
   L.ascale = take(T * 4);
   L.qkv = take(T * 3 * H * ab);
@@ -192,7 +196,7 @@ struct tte_model {
   uint8_t* ws;
   int device;
   // carved workspace
-  float* x;
+  void* x;  // residual stream [T, H], format x_kind(precision)
   void* xa;
   float* ascale;
   void* qkv;
@@ -352,13 +356,19 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
   const tte_config& c = m->cfg;
   const int P = c.precision, H = c.hidden, I = c.intermediate, nh = c.n_heads;
   const int act = P == TTE_BF16 ? O_BF16 : O_F32;  // format of qkv / o / y
-  const size_t state_bytes = (size_t)T * H * 4;
+  const int xk = x_kind(P);                          // format of the residual stream
+  // a trace copies x (converted to fp32 if it is bf16)
+  auto dump = [&](int k) {
+    float* dst = d_states + (size_t)k * T * H;
+    if (xk == O_F32) (void)hipMemcpyAsync(dst, m->x, (size_t)T * H * 4, hipMemcpyDeviceToDevice, s);
+    else launch_ln(m->x, xk, nullptr, T, H, 0.f, O_F32, dst, nullptr, s);
+  };
   {
     ProfScope ps(m, TTE_K_EMBED, s);
     launch_embed_ln(P == TTE_INT4 ? TTE_INT8 : P, d_ids, io, T, m->w.tok_emb, m->w.tok_emb_scale, c.vocab,
-                    m->w.emb_norm, c.ln_eps, H, m->d_off, B, m->x, m->seg, s);
+                    m->w.emb_norm, c.ln_eps, H, m->d_off, B, m->x, xk, m->seg, s);
   }
-  if (d_states) (void)hipMemcpyAsync(d_states, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
+  if (d_states) dump(0);
 
   // With TTE_FLAG_SPLIT_K the residual products of a short pack run split-K
   // (their H-wide outputs give fewer tiles than the compute units can hold);
@@ -373,17 +383,18 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
   for (int l = 0; l < n_run; ++l) {
     const tte_layer_weights& LW = m->layers[l];
     const int glob = (l % c.global_every) == 0;
-    // attention sub-layer input: no norm on layer 0
+    // attention sub-layer input: no norm on layer 0, so the product reads
+    // x itself where x is already in the operand format
     const void* a_in = m->xa;
-    if (P == TTE_FP32 && l == 0) {
+    if (l == 0 && xk == in_fmt) {
       a_in = m->x;
     } else if (pending) {
       ProfScope ps(m, TTE_K_NORM, s);
-      launch_resid_ln(m->x, m->kpart, o2_splits, LW.attn_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
+      launch_resid_ln(m->x, xk, m->kpart, o2_splits, LW.attn_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
       pending = false;
     } else {
       ProfScope ps(m, integer && l == 0 ? TTE_K_QUANT : TTE_K_NORM, s);
-      launch_ln(m->x, l == 0 ? nullptr : LW.attn_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
+      launch_ln(m->x, xk, l == 0 ? nullptr : LW.attn_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
     }
     {
       ProfScope ps(m, TTE_K_GEMM_QKV, s);
@@ -404,13 +415,13 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
     {
       ProfScope ps(m, TTE_K_GEMM_O, s);
       if (o_splits > 1) launch_gemm_splitk(P, o_in, m->ascale, LW.wo, LW.wo_scale, T, H, H, o_splits, m->kpart, s);
-      else launch_gemm(P, E_RESID, o_in, m->ascale, LW.wo, LW.wo_scale, T, H, H, m->x, O_F32, s);
+      else launch_gemm(P, E_RESID, o_in, m->ascale, LW.wo, LW.wo_scale, T, H, H, m->x, xk, s);
     }
     {
       ProfScope ps(m, TTE_K_NORM, s);
       if (o_splits > 1)
-        launch_resid_ln(m->x, m->kpart, o_splits, LW.mlp_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
-      else launch_ln(m->x, LW.mlp_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
+        launch_resid_ln(m->x, xk, m->kpart, o_splits, LW.mlp_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
+      else launch_ln(m->x, xk, LW.mlp_norm, T, H, c.ln_eps, in_fmt, m->xa, m->ascale, s);
     }
     {
       ProfScope ps(m, TTE_K_GEMM_GEGLU, s);
@@ -428,23 +439,23 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
         launch_gemm_splitk(P, y_in, m->ascale, LW.wo2, LW.wo2_scale, T, H, I, o2_splits, m->kpart, s);
         pending = true;
       } else {
-        launch_gemm(P, E_RESID, y_in, m->ascale, LW.wo2, LW.wo2_scale, T, H, I, m->x, O_F32, s);
+        launch_gemm(P, E_RESID, y_in, m->ascale, LW.wo2, LW.wo2_scale, T, H, I, m->x, xk, s);
       }
     }
     if (pending && (d_states || l + 1 == n_run)) {
       // a trace copies x, and pooling reads it: apply the partials now
       ProfScope ps(m, TTE_K_NORM, s);
-      launch_resid_ln(m->x, m->kpart, o2_splits, nullptr, T, H, c.ln_eps, -1, nullptr, nullptr, s);
+      launch_resid_ln(m->x, xk, m->kpart, o2_splits, nullptr, T, H, c.ln_eps, -1, nullptr, nullptr, s);
       pending = false;
     }
-    if (d_states) (void)hipMemcpyAsync(d_states + (size_t)(l + 1) * T * H, m->x, state_bytes, hipMemcpyDeviceToDevice, s);
+    if (d_states) dump(l + 1);
   }
   if (n_run == c.n_layers && d_tok) {
     ProfScope ps(m, TTE_K_NORM, s);
-    launch_ln(m->x, m->w.final_norm, T, H, c.ln_eps, O_F32, d_tok, nullptr, s, io);
+    launch_ln(m->x, xk, m->w.final_norm, T, H, c.ln_eps, O_F32, d_tok, nullptr, s, io);
   } else if (n_run == c.n_layers) {
     ProfScope ps(m, TTE_K_POOL, s);
-    launch_pool(m->x, m->w.final_norm, c.ln_eps, H, m->d_off, m->d_unit, B, n_units, m->partial, d_out, s, io);
+    launch_pool(m->x, xk, m->w.final_norm, c.ln_eps, H, m->d_off, m->d_unit, B, n_units, m->partial, d_out, s, io);
   }
 }
 
@@ -737,7 +748,7 @@ tte_status tte_create(const tte_config* cfg, const tte_weights* w, void* d_works
   m->ws = reinterpret_cast<uint8_t*>(d_workspace);
   (void)hipGetDevice(&m->device);
   uint8_t* b = m->ws;
-  m->x = reinterpret_cast<float*>(b + L.x);
+  m->x = b + L.x;
   m->xa = b + L.xa;
   m->ascale = reinterpret_cast<float*>(b + L.ascale);
   m->qkv = b + L.qkv;
@@ -855,7 +866,7 @@ tte_status tte_op_layernorm(const float* d_x, const float* d_gamma, int32_t rows
   if (!d_x || !d_out || (out_kind == TTE_OUT_I8 && !d_scale)) return fail(TTE_E_INVALID, "NULL buffer");
   if (d_gamma && !(eps > 0.f)) return fail(TTE_E_INVALID, "eps must be > 0");
   (void)hipGetLastError();
-  launch_ln(d_x, d_gamma, rows, width, eps, out_kind, d_out, d_scale, reinterpret_cast<hipStream_t>(stream));
+  launch_ln(d_x, O_F32, d_gamma, rows, width, eps, out_kind, d_out, d_scale, reinterpret_cast<hipStream_t>(stream));
   return hip_check(hipGetLastError(), "kernel launch");
 }
 
@@ -879,7 +890,8 @@ tte_status tte_op_gemm(int32_t precision, int32_t epilogue, const void* d_a, con
   if (epilogue == TTE_EPI_GEGLU ? (N % 64 != 0) : (N % 128 != 0))
     return fail(TTE_E_UNSUPPORTED, "N must be a multiple of 128 (64 for GEGLU)");
   if (out_kind != TTE_OUT_F32 && out_kind != TTE_OUT_BF16) return fail(TTE_E_INVALID, "out_kind must be F32 or BF16");
-  if (epilogue == TTE_EPI_RESIDUAL && out_kind != TTE_OUT_F32) return fail(TTE_E_INVALID, "RESIDUAL needs fp32 C");
+  if (epilogue == TTE_EPI_RESIDUAL && out_kind != TTE_OUT_F32 && precision != TTE_BF16)
+    return fail(TTE_E_INVALID, "RESIDUAL needs fp32 C (bf16 C with TTE_BF16 only)");
   if (!weight_offsets_fit(precision, epilogue == TTE_EPI_GEGLU ? 2 * (int64_t)N : N, K))
     return fail(TTE_E_UNSUPPORTED, "W is 4 GiB or larger (the kernels address its rows with 32-bit byte offsets)");
   if (M == 0) return TTE_OK;
@@ -922,7 +934,7 @@ tte_status tte_op_resid_ln(float* d_x, const float* d_partials, int32_t splits, 
     return fail(TTE_E_INVALID, "NULL buffer");
   if (d_gamma && !(eps > 0.f)) return fail(TTE_E_INVALID, "eps must be > 0");
   (void)hipGetLastError();
-  launch_resid_ln(d_x, d_partials, splits, d_gamma, rows, width, eps, out_kind, d_out, d_scale,
+  launch_resid_ln(d_x, O_F32, d_partials, splits, d_gamma, rows, width, eps, out_kind, d_out, d_scale,
                   reinterpret_cast<hipStream_t>(stream));
   return hip_check(hipGetLastError(), "kernel launch");
 }
@@ -996,7 +1008,7 @@ tte_status tte_op_pool(tte_model* m, const float* d_x, int32_t n_tokens, const i
   int n_units = 0;
   st = upload_pack(m, h_offsets, n_texts, &n_units, s);
   if (st != TTE_OK) return st;
-  launch_pool(d_x, m->w.final_norm, m->cfg.ln_eps, m->cfg.hidden, m->d_off, m->d_unit, n_texts, n_units, m->partial,
+  launch_pool(d_x, O_F32, m->w.final_norm, m->cfg.ln_eps, m->cfg.hidden, m->d_off, m->d_unit, n_texts, n_units, m->partial,
               d_out, s);
   return hip_check(hipGetLastError(), "kernel launch");
 }
@@ -1029,7 +1041,7 @@ tte_status tte_op_pool_static(tte_model* m, const float* d_x, int32_t n_tokens, 
   int* d_off = reinterpret_cast<int*>(base);
   st = stage_offsets_to(m, h_offsets, n_texts, (int)n_units, d_off, s);
   if (st != TTE_OK) return st;
-  launch_pool(d_x, m->w.final_norm, m->cfg.ln_eps, H, d_off, d_off + (n_texts + 1), n_texts, (int)n_units,
+  launch_pool(d_x, O_F32, m->w.final_norm, m->cfg.ln_eps, H, d_off, d_off + (n_texts + 1), n_texts, (int)n_units,
               reinterpret_cast<float*>(base + head), d_out, s);
   return hip_check(hipGetLastError(), "kernel launch");
 }
