@@ -164,8 +164,11 @@ def class_work(cfg, packs):
     w = {k: (f(H, I) * T * Lyr, "TFLOP/s", gemm_peak) for k, f in GEMM_CLASSES.items()}
     w["attn_global"] = (pg * per_pair * n_glob, "TFLOP/s", attn_peak)
     w["attn_local"] = (pl * per_pair * (Lyr - n_glob), "TFLOP/s", attn_peak)
-    w["norm"] = (2 * Lyr * T * H * (4 + out_b), "GB/s", None)  # read fp32 rows, write the GEMM operand
-    w["pool"] = (T * H * 4, "GB/s", None)
+    x_b = 2 if cfg.precision == "bf16" else 4  # element bytes of the residual stream
+    # 2 L - 1 norms (layer 0's attention input is the embedding norm's
+    # output): read x rows, write the GEMM operand
+    w["norm"] = ((2 * Lyr - 1) * T * H * (x_b + out_b), "GB/s", None)
+    w["pool"] = (T * H * x_b, "GB/s", None)
     return w
 
 
