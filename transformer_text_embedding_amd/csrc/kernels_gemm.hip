@@ -782,7 +782,14 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
 // Tile choice, measured on MI355X (bf16, the encoder's shapes at 1.9k and
 // 16k tokens; 2 LDS stages of 128-byte K tiles unless noted):
 //  * T256: 256 x 256, 8 waves of 128 x 64 (one block per CU): wide products
-//    with >= 512 such tiles, and the residual products of >= 8k rows;
+//    with >= 512 such tiles, and the residual products of >= 8k rows whose
+//    width is no multiple of 192;
+//  * T256N192: 256 x 192, 8 waves of 128 x 48 (one block per CU): the
+//    residual products of >= 8k rows otherwise: 768 columns make 4 tiles
+//    a row block instead of 3, so 16k rows fill the 256 CUs exactly
+//    (192 blocks of 256 x 256 left 64 idle): 4 texts of 4096 tokens, Wo
+//    0.85 -> 0.74 and Wo2 2.23 -> 1.92 ms per pass, 1.418 -> 1.457M
+//    tokens/s (interleaved runs);
 //  * T128W8 / T192W8: 128 x 128 or 192 x 128, 8 waves of 32 x 64 or
 //    48 x 64 (two blocks per CU): every other product (QKV always, GeGLU
 //    below the T256 size, the residual products below 8k rows); GeGLU takes
@@ -805,7 +812,7 @@ void go_prec(int epi, const void* A, const float* a_scale, const void* W, const 
 //  * int8 (its scale staging feeds 32 W rows per wave) and fp32 (measured
 //    slower with 8 waves: GeGLU at 957 tokens 54% against 64% of the fp32
 //    peak) keep 4-wave tiles: 128 x 128 once there are >= 1024 such tiles.
-enum TileCfg { T32, T64, T64L, T128, T128W8, T192W8, T256 };
+enum TileCfg { T32, T64, T64L, T128, T128W8, T192W8, T256, T256N192 };
 
 TileCfg pick_tiles(int prec, int epi, int M, int n_cols, int K) {
   const long tiles128 = (long)((M + 127) / 128) * (n_cols / 128);
@@ -813,6 +820,7 @@ TileCfg pick_tiles(int prec, int epi, int M, int n_cols, int K) {
   if (prec != P_BF16) {
     if (tiles128 >= 1024) return T128;
   } else {
+    if (epi == E_RESID && M >= 8192 && n_cols % 192 == 0) return T256N192;
     if (epi == E_RESID ? (M >= 8192 && n_cols % 256 == 0) : (tiles256 >= 512 && n_cols % 256 == 0)) return T256;
     const long c128 = ((tiles128 + 255) / 256) * 128;
     const long c192 = (((long)((M + 191) / 192) * (n_cols / 128) + 255) / 256) * 192;
@@ -854,6 +862,12 @@ void launch_prec(int epi, const void* A, const float* a_scale, const void* W, co
       break;
     case T256:
       if constexpr (PREC == P_BF16) go_prec<PREC, 8, 2, 2, 4>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s);
+      break;
+    case T256N192:  // residual products only
+      if constexpr (PREC == P_BF16) {
+        if (out_kind == O_BF16) go<PREC, E_RESID, O_BF16, 8, 3, 2, 2, 4>(A, a_scale, W, w_scale, M, N, K, C, s);
+        else go<PREC, E_RESID, O_F32, 8, 3, 2, 2, 4>(A, a_scale, W, w_scale, M, N, K, C, s);
+      }
       break;
     default: go_prec<PREC, 2, 2>(epi, A, a_scale, W, w_scale, M, N, K, C, out_kind, s); break;
   }
