@@ -28,8 +28,11 @@
 // the matrix-core output layout puts one query per lane column: each lane's
 // scores of its query are directly the B operand of the P*V product, and the
 // running max / sum / rescale of a query stay in the lanes that hold it.
-// Softmax uses exp2 with log2(e)/8 folded into one multiply; the output and
-// sum are rescaled only on tiles where some lane's running max moved.  fp32
+// Softmax uses exp2 with log2(e)/8 folded into one multiply, against a
+// reference max per query that moves only when a score exceeds it by more
+// than 8 in log2 units (so P <= 2^8; softmax is unchanged by the reference
+// it is taken against): the output and sum are rescaled only on the rare
+// tiles where that happens for some lane of the wave.  fp32
 // variant: v_mfma_f32_16x16x4_f32; bf16 variant: v_mfma_f32_16x16x32_bf16
 // with P rounded to bf16, its per-query sum taken on the matrix cores too
 // (against an all-ones block, so numerator and denominator use the same
@@ -248,6 +251,9 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
     lacc[qt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
+  // 8 in log2 units, as a difference of raw scores: P stays <= 256 (no
+  // overflow in fp32 or bf16; bf16 rounds P to the same relative precision)
+  const float lazy_gap = 8.f / scale_log2;
   for (int t = 0; t < C::STAGES - 1 && t < n_tiles; ++t) issue(t);
   for (int t = 0; t < n_tiles; ++t) {
     // this wave's loads of tile t (and the Q loads before them) are done
@@ -314,20 +320,23 @@ __global__ __launch_bounds__(256) void k_attn(const void* __restrict__ qk, const
 #pragma unroll
       for (int i = 0; i < 16; ++i) mloc = fmaxf(mloc, sv[qt][i]);
       mloc = rows_max(mloc);
+      // the reference max m_run moves to the running max only when that
+      // exceeds it by more than lazy_gap (never while every score seen is
+      // masked); the output and sum are then rescaled by exp2 of a
+      // difference <= 0 (or -inf, giving 0), on the lanes that move
       const float m_new = fmaxf(m_run[qt], mloc);
-      const float m_use = m_new == NEG_INF ? 0.f : m_new;
-      // the output and sum are rescaled only when some lane's running max
-      // moved (otherwise the factor is exactly 1)
-      if (__any(m_new != m_run[qt])) {
-        // every exponent below is <= 0 (or -inf): the hardware exp2 suffices
-        const float alpha = __builtin_amdgcn_exp2f((m_run[qt] - m_use) * scale_log2);
+      const bool move = m_new > m_run[qt] + lazy_gap;
+      if (__any(move)) {
+        const float m_use = m_new == NEG_INF ? 0.f : m_new;
+        const float alpha = move ? __builtin_amdgcn_exp2f((m_run[qt] - m_use) * scale_log2) : 1.f;
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) oacc[qt][dt] *= alpha;
         if constexpr (PREC == P_F32) l_run[qt] *= alpha;
         else lacc[qt] *= alpha;
+        m_run[qt] = move ? m_new : m_run[qt];
       }
-      m_run[qt] = m_new;
-      const float mb = m_use * scale_log2;
+      // exponents <= 8 (scores at most lazy_gap above the reference)
+      const float mb = (m_run[qt] == NEG_INF ? 0.f : m_run[qt]) * scale_log2;
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[qt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(sv[qt][i], scale_log2, -mb));
       if constexpr (PREC == P_F32) {
