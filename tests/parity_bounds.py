@@ -18,7 +18,8 @@ exact softmax weights and O_i = sum_j w_ij v_j:
     C_idd' = sum_j w_ij k_jd (v_jd' - O_id');
   - K errors: (1/8) sum_d q_id dk_jd, independent over j and d: variance
     (u^2/192) sum_j w_ij^2 (v_jd' - O_id')^2 sum_d q_id^2 k_jd^2;
-* P errors: P_j (1 + eta_j), and the kernel divides by the sum of the same
+* P errors: P_j (1 + eta_j) (P taken against any reference max: the
+  rounding is relative), and the kernel divides by the sum of the same
   rounded P, so O moves by sum_j w_ij eta_j (v_j - O_i): variance
   (u^2/3) sum_j w_ij^2 (v_jd' - O_id')^2;
 * the final rounding of O adds at most u |O|; fp32 sums over n keys add at
@@ -106,7 +107,12 @@ def attention_bf16_bound(qkv, offsets, n_heads, head_dim, is_global, window, rop
 def attention_bf16_emulated(qkv, offsets, n_heads, head_dim, is_global, window, rope_base):
     """The bf16 kernel's roundings replayed in NumPy (for checking the bound
     on the CPU): Q, K after RoPE to bf16, scores and sums in fp32, P to bf16
-    with the row sum taken over the rounded P, O to bf16."""
+    with the row sum taken over the rounded P, O to bf16.  P is taken here
+    against the row max; the kernel takes it against a reference that lags
+    the running max by less than 2^8 (P <= 256), which scales P by a
+    factor the softmax divides out again and leaves each rounding of P
+    within the same relative u, the only property of P's rounding the
+    bound uses."""
     q, k, v = _heads(qkv, offsets, n_heads, head_dim, rope_base)
     q, k = bf16_round(q), bf16_round(k)
     T = q.shape[0]
