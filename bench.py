@@ -348,6 +348,9 @@ def main():
 # workload as a single caller would run it: one stream, the down-projection
 # split over K so that a lone pack fills the CUs (lower latency per pack).
 SECONDARY = [("full_fp32_957", "full_fp32_957", 30, None, False),
+             # the same lone pack in the library's latency mode (one caller,
+             # one call at a time: the residual products split over K)
+             ("full_fp32_957_split_k", "full_fp32_957", 30, None, True),
              ("full_bf16_4x4096", "full_bf16_4x4096", 10, None, False),
              ("full_int8_packs2048", "full_int8_packs2048", 10, None, False),
              ("full_int4_packs2048", "full_int4_packs2048", 10, None, False),
