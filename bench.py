@@ -240,7 +240,7 @@ def main():
                     help="only copy a MIB-sized fp32 buffer 5 times with torch (known bytes, for HBM counter scaling)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {a.gpus}).",
+        print(f"bench.py measures one GPU: the library has no multi-GPU path (asked for --gpus {a.gpus}).",
               file=sys.stderr)
         sys.exit(2)
 
