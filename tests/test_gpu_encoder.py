@@ -120,6 +120,22 @@ def test_tiny_layer_trace_matches_oracle(tiny_models):
     np.testing.assert_allclose(host(out), oracle.encode(cfg.as_dict(), w, pack.ids, pack.offsets), atol=1e-4)
 
 
+def test_tiny_bf16_stream_holds_bf16_values(tiny_models):
+    """In the bf16 mode the residual stream is stored in bf16: every state a
+    trace returns (fp32) is a bf16 value exactly (low 16 bits zero), and the
+    states follow the oracle's to the bf16 stream's precision."""
+    cfg, w, m = tiny_models["bf16"]
+    pack = ti.make_packs("tiny_fp32")[0]
+    states, _ = m.trace(dev(pack.ids), pack.offsets, cfg.layers)
+    st = host(states)
+    assert np.all((st.view(np.uint32) & 0xFFFF) == 0)
+    ref = oracle.encode_layers(cfg.as_dict(), w, pack.ids, pack.offsets)
+    for l, r in enumerate(ref):
+        cos = row_cosines(st[l], r)
+        say(f"  bf16 state {l}: token cos min {cos.min():.8f}")
+        assert cos.min() >= 1 - 1e-4, (l, cos.min())
+
+
 @pytest.mark.parametrize("precision", ["fp32", "bf16", "int8"])
 def test_packed_equals_alone_and_deterministic(tiny_models, precision):
     cfg, w, m = tiny_models[precision]

@@ -129,9 +129,10 @@ void launch_resid_ln(void* x, int x_kind, const float* partials, int splits, con
 
 // QKV projection with the RoPE / transposed-V epilogue: writes rotated Q
 // and K into qkv [M, 3H] (columns 0 .. 2H-1) and V into qo.vt.  Requires
-// the per-token text bounds of the pack in qo.seg.
+// the per-token text bounds of the pack in qo.seg.  fill (bf16, the
+// latency mode): tiles that fill the chip for one pack on its own.
 void launch_gemm_qkv(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M,
-                     int K, void* qkv, int out_kind, const QkvOut& qo, hipStream_t s);
+                     int K, void* qkv, int out_kind, const QkvOut& qo, hipStream_t s, bool fill = false);
 
 // The same RoPE and V transposition from an unrotated qkv [T, 3H] (for the
 // single-kernel attention entry point).

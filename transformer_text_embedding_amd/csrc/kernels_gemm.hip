@@ -875,9 +875,16 @@ void launch_prec(int epi, const void* A, const float* a_scale, const void* W, co
 
 template <int PREC, int OUT>
 void launch_qkv_prec(const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int K,
-                     void* qkv, const QkvOut& qo, hipStream_t s) {
+                     void* qkv, const QkvOut& qo, hipStream_t s, bool fill) {
   const int N = 3 * qo.hidden;
-  if constexpr (PREC != P_BF16) {
+  if (fill && M <= 4096) {
+    // a lone caller (the latency mode): 4-wave 64 x 128 tiles, ~540 blocks
+    // at 1.9k rows instead of 180 of 192 x 128, which leave 76 CUs idle
+    // when no other pack's kernels fill them (QKV 28.8 -> 27.0 ms per
+    // single-stream step of 64 packs; with four streams the larger tiles
+    // stay ahead)
+    go<PREC, E_QKV, OUT, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
+  } else if constexpr (PREC != P_BF16) {
     if (pick_tiles(PREC, E_QKV, M, N, K) == T128) go<PREC, E_QKV, OUT, 4, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
     else go<PREC, E_QKV, OUT, 2, 4, 2>(A, a_scale, W, w_scale, M, N, K, qkv, s, qo);
   } else if (pick_tiles(PREC, E_QKV, M, N, K) == T192W8) {
@@ -941,13 +948,13 @@ void launch_gemm_splitk(int prec, const void* A, const float* a_scale, const voi
 }
 
 void launch_gemm_qkv(int prec, const void* A, const float* a_scale, const void* W, const float* w_scale, int M, int K,
-                     void* qkv, int out_kind, const QkvOut& qo, hipStream_t s) {
+                     void* qkv, int out_kind, const QkvOut& qo, hipStream_t s, bool fill) {
   if (M <= 0) return;
-  if (prec == P_F32) launch_qkv_prec<P_F32, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
-  else if (prec == P_BF16 && out_kind == O_BF16) launch_qkv_prec<P_BF16, O_BF16>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
-  else if (prec == P_BF16) launch_qkv_prec<P_BF16, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
-  else if (prec == P_I8) launch_qkv_prec<P_I8, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
-  else launch_qkv_prec<P_I4, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s);
+  if (prec == P_F32) launch_qkv_prec<P_F32, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s, false);
+  else if (prec == P_BF16 && out_kind == O_BF16) launch_qkv_prec<P_BF16, O_BF16>(A, a_scale, W, w_scale, M, K, qkv, qo, s, fill);
+  else if (prec == P_BF16) launch_qkv_prec<P_BF16, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s, false);
+  else if (prec == P_I8) launch_qkv_prec<P_I8, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s, false);
+  else launch_qkv_prec<P_I4, O_F32>(A, a_scale, W, w_scale, M, K, qkv, qo, s, false);
 }
 
 }  // namespace tte

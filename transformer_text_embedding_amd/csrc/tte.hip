@@ -399,7 +399,7 @@ void enqueue_pass(tte_model* m, const int32_t* d_ids, const PackIO* io, int32_t 
     {
       ProfScope ps(m, TTE_K_GEMM_QKV, s);
       const QkvOut qo{m->seg, glob ? m->cosg : m->cosl, glob ? m->sing : m->sinl, m->vt, m->L.vt_stride, H};
-      launch_gemm_qkv(P, a_in, m->ascale, LW.wqkv, LW.wqkv_scale, T, H, m->qkv, act, qo, s);
+      launch_gemm_qkv(P, a_in, m->ascale, LW.wqkv, LW.wqkv_scale, T, H, m->qkv, act, qo, s, split);
     }
     {
       ProfScope ps(m, glob ? TTE_K_ATTN_GLOBAL : TTE_K_ATTN_LOCAL, s);
